@@ -1,0 +1,260 @@
+"""MI355X (gfx950) NVFP4 weight-only GEMM library -- Python binding.
+
+The compute lives in ``libnvfp4.so`` (hand-written HIP kernels behind the C
+ABI declared in ``include/nvfp4.h``).  This module only marshals torch tensors
+(device memory and streams) into that ABI.  There is no fallback: if the
+library is missing, importing the binding's functions raises.
+
+Low-level functions carry the C names (``nvfp4_quantize``, ``nvfp4_gemm``,
+``nvfp4_grouped_gemm``, ...) and take every buffer explicitly; ``quantize``,
+``gemm`` and ``grouped_gemm`` allocate outputs and a cached workspace.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
+
+OK = 0
+STATUS_NAMES = {0: "NVFP4_OK", 1: "NVFP4_ERR_INVALID_ARGUMENT", 2: "NVFP4_ERR_MISALIGNED",
+                3: "NVFP4_ERR_UNSUPPORTED", 4: "NVFP4_ERR_WORKSPACE", 5: "NVFP4_ERR_HIP"}
+OUT_BF16 = 0
+OUT_F32 = 1
+DSTATUS_NONFINITE = 1
+DSTATUS_BAD_OFFSETS = 2
+MAX_EXPERTS = 1024
+
+EXPORTED = [
+    "nvfp4_quantize", "nvfp4_gemm", "nvfp4_grouped_gemm", "nvfp4_quantize_workspace_size",
+    "nvfp4_gemm_workspace_size", "nvfp4_grouped_gemm_workspace_size",
+    "nvfp4_workspace_counter_bytes", "nvfp4_workspace_init", "nvfp4_status_string",
+    "nvfp4_version",
+]
+
+_lib = None
+_lock = threading.Lock()
+
+
+class NVFP4Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__("%s: %s" % (what, STATUS_NAMES.get(status, str(status))))
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libnvfp4.so and declare its C signatures.  Raises OSError if the
+    library has not been built (``python -m block_scaled_fp4_nibble_amd.build``)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise OSError("libnvfp4.so not found at %s; build it with "
+                          "`python -m block_scaled_fp4_nibble_amd.build`" % path)
+        lib = ctypes.CDLL(path)
+        P, I64, SZ, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+        lib.nvfp4_quantize.argtypes = [P, I64, I64, I64, P, P, P, P, P, SZ, P]
+        lib.nvfp4_quantize.restype = I32
+        lib.nvfp4_gemm.argtypes = [P, I64, I64, I64, P, P, P, P, I32, P, SZ, P]
+        lib.nvfp4_gemm.restype = I32
+        lib.nvfp4_grouped_gemm.argtypes = [P, I64, P, I64, I64, I64, P, P, P, P, I32, P, P, SZ, P]
+        lib.nvfp4_grouped_gemm.restype = I32
+        lib.nvfp4_quantize_workspace_size.argtypes = [I64, I64, I64]
+        lib.nvfp4_quantize_workspace_size.restype = SZ
+        lib.nvfp4_gemm_workspace_size.argtypes = [I64, I64, I64]
+        lib.nvfp4_gemm_workspace_size.restype = SZ
+        lib.nvfp4_grouped_gemm_workspace_size.argtypes = [I64, I64, I64, I64]
+        lib.nvfp4_grouped_gemm_workspace_size.restype = SZ
+        lib.nvfp4_workspace_counter_bytes.argtypes = []
+        lib.nvfp4_workspace_counter_bytes.restype = SZ
+        lib.nvfp4_workspace_init.argtypes = [P, SZ, P]
+        lib.nvfp4_workspace_init.restype = I32
+        lib.nvfp4_status_string.argtypes = [I32]
+        lib.nvfp4_status_string.restype = ctypes.c_char_p
+        lib.nvfp4_version.argtypes = []
+        lib.nvfp4_version.restype = I32
+        _lib = lib
+        return lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(status: int, what: str):
+    if status != OK:
+        raise NVFP4Error(status, what)
+
+
+# ---- raw C entry points (explicit buffers) ---------------------------------
+
+def nvfp4_quantize(w, batch, n, k, packed, scales, global_scale, d_status, workspace,
+                   ws_bytes, stream=None):
+    return load_library().nvfp4_quantize(_ptr(w), batch, n, k, _ptr(packed), _ptr(scales),
+                                         _ptr(global_scale), _ptr(d_status), _ptr(workspace),
+                                         ws_bytes, _stream(stream))
+
+
+def nvfp4_gemm(x, m, n, k, packed, scales, global_scale, y, out, workspace, ws_bytes,
+               stream=None):
+    return load_library().nvfp4_gemm(_ptr(x), m, n, k, _ptr(packed), _ptr(scales),
+                                     _ptr(global_scale), _ptr(y), out, _ptr(workspace), ws_bytes,
+                                     _stream(stream))
+
+
+def nvfp4_grouped_gemm(x, rows, offsets, num_experts, n, k, packed, scales, global_scales, y,
+                       out, d_status, workspace, ws_bytes, stream=None):
+    return load_library().nvfp4_grouped_gemm(_ptr(x), rows, _ptr(offsets), num_experts, n, k,
+                                             _ptr(packed), _ptr(scales), _ptr(global_scales),
+                                             _ptr(y), out, _ptr(d_status), _ptr(workspace),
+                                             ws_bytes, _stream(stream))
+
+
+def nvfp4_quantize_workspace_size(batch, n, k) -> int:
+    return load_library().nvfp4_quantize_workspace_size(batch, n, k)
+
+
+def nvfp4_gemm_workspace_size(m, n, k) -> int:
+    return load_library().nvfp4_gemm_workspace_size(m, n, k)
+
+
+def nvfp4_grouped_gemm_workspace_size(rows, num_experts, n, k) -> int:
+    return load_library().nvfp4_grouped_gemm_workspace_size(rows, num_experts, n, k)
+
+
+def nvfp4_workspace_counter_bytes() -> int:
+    return load_library().nvfp4_workspace_counter_bytes()
+
+
+def nvfp4_workspace_init(workspace, ws_bytes, stream=None):
+    return load_library().nvfp4_workspace_init(_ptr(workspace), ws_bytes, _stream(stream))
+
+
+def nvfp4_status_string(status: int) -> str:
+    return load_library().nvfp4_status_string(status).decode()
+
+
+def nvfp4_version() -> int:
+    return load_library().nvfp4_version()
+
+
+# ---- convenience layer --------------------------------------------------------
+
+@dataclass
+class QuantizedWeight:
+    """NVFP4 weight: packed [.., n, k/2] uint8, scales [.., n, k/16] uint8
+    (E4M3 bits), global_scale [batch] float32 -- all on one device."""
+    packed: torch.Tensor
+    scales: torch.Tensor
+    global_scale: torch.Tensor
+
+    @property
+    def n(self) -> int:
+        return self.packed.shape[-2]
+
+    @property
+    def k(self) -> int:
+        return self.packed.shape[-1] * 2
+
+
+class Workspace:
+    """Grow-only device workspace whose counter region is zeroed once at
+    allocation (the kernels leave it zeroed after every call)."""
+
+    def __init__(self):
+        self._buf = {}
+
+    def get(self, nbytes: int, device, stream=None):
+        if nbytes == 0:
+            return None
+        key = torch.device(device).index
+        buf = self._buf.get(key)
+        if buf is None or buf.numel() < nbytes:
+            buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+            _check(nvfp4_workspace_init(buf, buf.numel(), stream), "nvfp4_workspace_init")
+            self._buf[key] = buf
+        return buf
+
+
+_gemm_ws = Workspace()
+_quant_ws = Workspace()
+
+
+def _bf16_2d_or_3d(t, name):
+    if t.dtype != torch.bfloat16 or not t.is_cuda:
+        raise TypeError("%s must be a CUDA/HIP bfloat16 tensor" % name)
+    return t.contiguous()
+
+
+def quantize(w: torch.Tensor, d_status: torch.Tensor | None = None, stream=None) -> QuantizedWeight:
+    """Encode BF16 weights [n, k] or [batch, n, k] to NVFP4 on the GPU."""
+    w = _bf16_2d_or_3d(w, "w")
+    squeeze = w.dim() == 2
+    w3 = w.unsqueeze(0) if squeeze else w
+    if w3.dim() != 3:
+        raise ValueError("w must be [n, k] or [batch, n, k]")
+    b, n, k = w3.shape
+    dev = w.device
+    packed = torch.empty((b, n, k // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((b, n, k // 16), dtype=torch.uint8, device=dev)
+    g = torch.empty((b,), dtype=torch.float32, device=dev)
+    nbytes = nvfp4_quantize_workspace_size(b, n, k)
+    ws = _quant_ws.get(nbytes, dev, stream)
+    _check(nvfp4_quantize(w3, b, n, k, packed, scales, g, d_status, ws, nbytes, stream),
+           "nvfp4_quantize")
+    if squeeze:
+        return QuantizedWeight(packed[0], scales[0], g)
+    return QuantizedWeight(packed, scales, g)
+
+
+def gemm(x: torch.Tensor, qw: QuantizedWeight, out_dtype=torch.bfloat16,
+         out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """y [m, n] = x [m, k] (bf16) @ dequant(qw)^T."""
+    x = _bf16_2d_or_3d(x, "x")
+    m, k = x.shape
+    n = qw.packed.shape[-2]
+    if qw.packed.dim() != 2 or qw.k != k:
+        raise ValueError("weight must be a single [n, k/2] tensor matching x")
+    code = OUT_F32 if out_dtype == torch.float32 else OUT_BF16
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=x.device)
+    nbytes = nvfp4_gemm_workspace_size(m, n, k)
+    ws = _gemm_ws.get(nbytes, x.device, stream)
+    _check(nvfp4_gemm(x, m, n, k, qw.packed, qw.scales, qw.global_scale, out, code, ws,
+                      nbytes, stream), "nvfp4_gemm")
+    return out
+
+
+def grouped_gemm(x: torch.Tensor, offsets: torch.Tensor, qw: QuantizedWeight,
+                 out_dtype=torch.bfloat16, out: torch.Tensor | None = None,
+                 d_status: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Rows [offsets[e], offsets[e+1]) of x times expert e's weight.  Rows of
+    the output that belong to no expert are left as allocated."""
+    x = _bf16_2d_or_3d(x, "x")
+    rows, k = x.shape
+    if qw.packed.dim() != 3 or qw.k != k:
+        raise ValueError("weight must be [E, n, k/2] matching x")
+    E, n, _ = qw.packed.shape
+    if offsets.dtype != torch.int32 or offsets.numel() != E + 1 or not offsets.is_cuda:
+        raise ValueError("offsets must be a device int32 tensor of E+1 entries")
+    code = OUT_F32 if out_dtype == torch.float32 else OUT_BF16
+    if out is None:
+        out = torch.empty((rows, n), dtype=out_dtype, device=x.device)
+    nbytes = nvfp4_grouped_gemm_workspace_size(rows, E, n, k)
+    ws = _gemm_ws.get(nbytes, x.device, stream)
+    _check(nvfp4_grouped_gemm(x, rows, offsets.contiguous(), E, n, k, qw.packed, qw.scales,
+                              qw.global_scale, out, code, d_status, ws, nbytes, stream),
+           "nvfp4_grouped_gemm")
+    return out

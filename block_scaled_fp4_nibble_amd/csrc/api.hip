@@ -1,0 +1,200 @@
+// api.hip -- the C ABI of libnvfp4.so: argument checks, schedule choice and
+// launches.  Declarations and the contract are in include/nvfp4.h.
+//
+// Boundary lesson from the pages: a FP4 GEMM backend that launched, finished
+// and silently returned all zeros on unsupported hardware ("The SM120 FP4
+// GEMM Kernel Investigation", section "The Breaking Point: FlashInfer #2577")
+// and tile configurations that failed to initialize ("The Tile That Didn't
+// Fit", section "Why Tile Size Matters for FP4 Performance").  Here every
+// call either enqueues the complete computation or returns a non-OK status
+// without enqueuing anything.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <mutex>
+
+#include "nvfp4_internal.hpp"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+int g_cu_count[kMaxDevices] = {0};
+std::mutex g_mu;
+
+// Compute-unit count of the current device (cached per device).
+int cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (g_cu_count[dev] > 0) return g_cu_count[dev];
+  }
+  int v = 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      v <= 0)
+    v = 256;
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_cu_count[dev] = v;
+  return v;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kInt31 = (int64_t)1 << 31;
+
+nvfp4_status_t hip_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP; }
+
+nvfp4_status_t check_k(int64_t k) {
+  if (k < 16 || (k % 16) != 0 || k >= kInt31) return NVFP4_ERR_INVALID_ARGUMENT;
+  return NVFP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* nvfp4_status_string(nvfp4_status_t s) {
+  switch (s) {
+    case NVFP4_OK: return "NVFP4_OK";
+    case NVFP4_ERR_INVALID_ARGUMENT: return "NVFP4_ERR_INVALID_ARGUMENT";
+    case NVFP4_ERR_MISALIGNED: return "NVFP4_ERR_MISALIGNED";
+    case NVFP4_ERR_UNSUPPORTED: return "NVFP4_ERR_UNSUPPORTED";
+    case NVFP4_ERR_WORKSPACE: return "NVFP4_ERR_WORKSPACE";
+    case NVFP4_ERR_HIP: return "NVFP4_ERR_HIP";
+  }
+  return "NVFP4_ERR_UNKNOWN";
+}
+
+int nvfp4_version(void) { return 100; }
+
+size_t nvfp4_workspace_counter_bytes(void) { return nvfp4::kCounterBytes; }
+
+nvfp4_status_t nvfp4_workspace_init(void* workspace, size_t ws_bytes, void* stream) {
+  if (ws_bytes == 0) return NVFP4_OK;
+  if (workspace == nullptr) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (!aligned16(workspace)) return NVFP4_ERR_MISALIGNED;
+  const size_t bytes = std::min(ws_bytes, nvfp4::kCounterBytes) / 16 * 16;
+  return hip_status(
+      nvfp4::launch_fill_zero(workspace, bytes, reinterpret_cast<hipStream_t>(stream)));
+}
+
+// ---- quantize --------------------------------------------------------------
+
+size_t nvfp4_quantize_workspace_size(int64_t batch, int64_t n, int64_t k) {
+  if (batch <= 0 || n <= 0 || check_k(k) != NVFP4_OK) return 0;
+  const int parts = nvfp4::quantize_parts(n, k, cu_count());
+  return (size_t)batch * parts * sizeof(uint32_t);
+}
+
+nvfp4_status_t nvfp4_quantize(const void* w_bf16, int64_t batch, int64_t n, int64_t k,
+                              uint8_t* packed, uint8_t* scales, float* global_scale,
+                              uint32_t* d_status, void* workspace, size_t ws_bytes,
+                              void* stream) {
+  if (batch < 0 || n < 1 || check_k(k) != NVFP4_OK) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (batch == 0) return NVFP4_OK;
+  if (!w_bf16 || !packed || !scales || !global_scale) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (!aligned16(w_bf16) || !aligned16(packed) || !aligned16(scales) ||
+      (reinterpret_cast<uintptr_t>(global_scale) & 3u) != 0)
+    return NVFP4_ERR_MISALIGNED;
+  if (batch > 65535) return NVFP4_ERR_UNSUPPORTED;
+  if (n * (k / 16) / 256 >= kInt31) return NVFP4_ERR_UNSUPPORTED;
+  const int parts = nvfp4::quantize_parts(n, k, cu_count());
+  const size_t need = (size_t)batch * parts * sizeof(uint32_t);
+  if (workspace == nullptr || ws_bytes < need) return NVFP4_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return NVFP4_ERR_MISALIGNED;
+  return hip_status(nvfp4::launch_quantize(
+      static_cast<const uint16_t*>(w_bf16), batch, n, k, packed, scales, global_scale, d_status,
+      static_cast<uint32_t*>(workspace), parts, reinterpret_cast<hipStream_t>(stream)));
+}
+
+// ---- GEMM ------------------------------------------------------------------
+
+static nvfp4_status_t check_gemm_common(const void* x, int64_t rows, int64_t n, int64_t k,
+                                       const void* packed, const void* scales, const void* g,
+                                       const void* y, nvfp4_out_t out) {
+  if (rows < 0 || n < 1 || check_k(k) != NVFP4_OK) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (out != NVFP4_OUT_BF16 && out != NVFP4_OUT_F32) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (rows >= kInt31 || n >= kInt31) return NVFP4_ERR_UNSUPPORTED;
+  if (rows == 0) return NVFP4_OK;
+  if (!x || !packed || !scales || !g || !y) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (!aligned16(x) || !aligned16(packed) || !aligned16(scales) || !aligned16(y) ||
+      (reinterpret_cast<uintptr_t>(g) & 3u) != 0)
+    return NVFP4_ERR_MISALIGNED;
+  return NVFP4_OK;
+}
+
+size_t nvfp4_gemm_workspace_size(int64_t m, int64_t n, int64_t k) {
+  if (m <= 0 || n <= 0 || check_k(k) != NVFP4_OK) return 0;
+  return nvfp4::plan_gemm(m, 1, n, k, false, cu_count()).ws_bytes;
+}
+
+size_t nvfp4_grouped_gemm_workspace_size(int64_t rows, int64_t num_experts, int64_t n,
+                                         int64_t k) {
+  if (rows <= 0 || num_experts <= 0 || n <= 0 || check_k(k) != NVFP4_OK) return 0;
+  return nvfp4::plan_gemm(rows, num_experts, n, k, true, cu_count()).ws_bytes;
+}
+
+static nvfp4_status_t run_gemm(const void* x, int64_t rows, const int32_t* offsets, int64_t E,
+                               int64_t n, int64_t k, const uint8_t* packed,
+                               const uint8_t* scales, const float* g, void* y, nvfp4_out_t out,
+                               uint32_t* d_status, void* workspace, size_t ws_bytes,
+                               hipStream_t stream, bool grouped) {
+  const nvfp4::GemmPlan pl = nvfp4::plan_gemm(rows, E, n, k, grouped, cu_count());
+  if (pl.ws_bytes > 0) {
+    if (workspace == nullptr || ws_bytes < pl.ws_bytes) return NVFP4_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return NVFP4_ERR_MISALIGNED;
+  }
+  nvfp4::GemmParams p{};
+  p.x = static_cast<const uint16_t*>(x);
+  p.w = packed;
+  p.s = scales;
+  p.g = g;
+  p.offsets = offsets;
+  p.y = y;
+  p.counters = pl.splits > 1 ? static_cast<uint32_t*>(workspace) : nullptr;
+  p.partials = pl.splits > 1
+                   ? reinterpret_cast<float*>(static_cast<char*>(workspace) + nvfp4::kCounterBytes)
+                   : nullptr;
+  p.d_status = d_status;
+  p.rows = rows;
+  p.num_experts = (int32_t)E;
+  p.n = (int32_t)n;
+  p.k = (int32_t)k;
+  p.splits = pl.splits;
+  p.k_split = pl.k_split;
+  p.n_tiles = pl.n_tiles;
+  p.total_units = -1;
+  p.out_f32 = out == NVFP4_OUT_F32 ? 1 : 0;
+  return hip_status(nvfp4::launch_gemm(pl, p, stream));
+}
+
+nvfp4_status_t nvfp4_gemm(const void* x_bf16, int64_t m, int64_t n, int64_t k,
+                          const uint8_t* packed, const uint8_t* scales,
+                          const float* global_scale, void* y, nvfp4_out_t out, void* workspace,
+                          size_t ws_bytes, void* stream) {
+  nvfp4_status_t st = check_gemm_common(x_bf16, m, n, k, packed, scales, global_scale, y, out);
+  if (st != NVFP4_OK || m == 0) return st;
+  return run_gemm(x_bf16, m, nullptr, 1, n, k, packed, scales, global_scale, y, out, nullptr,
+                  workspace, ws_bytes, reinterpret_cast<hipStream_t>(stream), false);
+}
+
+nvfp4_status_t nvfp4_grouped_gemm(const void* x_bf16, int64_t rows,
+                                  const int32_t* expert_offsets, int64_t num_experts, int64_t n,
+                                  int64_t k, const uint8_t* packed, const uint8_t* scales,
+                                  const float* global_scales, void* y, nvfp4_out_t out,
+                                  uint32_t* d_status, void* workspace, size_t ws_bytes,
+                                  void* stream) {
+  if (num_experts < 1) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (num_experts > NVFP4_MAX_EXPERTS) return NVFP4_ERR_UNSUPPORTED;
+  nvfp4_status_t st =
+      check_gemm_common(x_bf16, rows, n, k, packed, scales, global_scales, y, out);
+  if (st != NVFP4_OK || rows == 0) return st;
+  if (expert_offsets == nullptr) return NVFP4_ERR_INVALID_ARGUMENT;
+  if ((reinterpret_cast<uintptr_t>(expert_offsets) & 3u) != 0) return NVFP4_ERR_MISALIGNED;
+  return run_gemm(x_bf16, rows, expert_offsets, num_experts, n, k, packed, scales,
+                  global_scales, y, out, d_status, workspace, ws_bytes,
+                  reinterpret_cast<hipStream_t>(stream), true);
+}
+
+}  // extern "C"

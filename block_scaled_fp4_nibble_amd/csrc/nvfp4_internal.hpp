@@ -1,0 +1,66 @@
+// nvfp4_internal.hpp -- launch interfaces shared by the C ABI and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/nvfp4.h"
+
+namespace nvfp4 {
+
+constexpr int kMaxExperts = NVFP4_MAX_EXPERTS;
+// Split-K tile counters live in the first kCounterBytes of a GEMM workspace.
+constexpr size_t kCounterBytes = 65536;
+constexpr int kMaxCounters = (int)(kCounterBytes / sizeof(uint32_t));
+
+// ---- quantize -----------------------------------------------------------
+int quantize_parts(int64_t n, int64_t k, int cu_count);
+hipError_t launch_quantize(const uint16_t* w, int64_t batch, int64_t n, int64_t k,
+                           uint8_t* packed, uint8_t* scales, float* gscale, uint32_t* d_status,
+                           uint32_t* partial, int parts, hipStream_t stream);
+
+// ---- GEMM ---------------------------------------------------------------
+// Column tile of one workgroup (4 waves x 4 MFMA column tiles x 16).
+constexpr int kGemmThreads = 256;
+constexpr int kBN = 256;
+// K covered by one staged activation chunk.
+constexpr int kKC = 256;
+
+struct GemmParams {
+  const uint16_t* x;        // [rows][k] bf16
+  const uint8_t* w;         // [E][n][k/2]
+  const uint8_t* s;         // [E][n][k/16]
+  const float* g;           // [E]
+  const int32_t* offsets;   // [E+1] on the device; nullptr: one segment of `rows`
+  void* y;                  // [rows][n]
+  float* partials;          // split-K partial tiles (nullptr when splits == 1)
+  uint32_t* counters;       // split-K arrival counters (nullptr when splits == 1)
+  uint32_t* d_status;       // may be nullptr
+  int64_t rows;
+  int32_t num_experts;
+  int32_t n;
+  int32_t k;
+  int32_t splits;           // K splits per output tile
+  int32_t k_split;          // K per split (multiple of 64 on the fast path, of 16 otherwise)
+  int32_t n_tiles;          // ceil(n / kBN)
+  int32_t total_units;      // exact for dense, -1 for grouped (computed on device)
+  int32_t out_f32;
+};
+
+struct GemmPlan {
+  int bm;        // rows per tile: 16, 32 or 64
+  int splits;
+  int k_split;
+  int n_tiles;
+  int max_tiles; // upper bound on output tiles (for counters / partials)
+  int grid;
+  bool fast;     // k % 64 == 0
+  size_t ws_bytes;
+};
+
+GemmPlan plan_gemm(int64_t rows, int64_t num_experts, int64_t n, int64_t k, bool grouped,
+                   int cu_count);
+hipError_t launch_gemm(const GemmPlan& plan, const GemmParams& p, hipStream_t stream);
+hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t stream);
+
+}  // namespace nvfp4

@@ -1,0 +1,162 @@
+/*
+ * nvfp4.h -- C ABI of the MI355X (gfx950) NVFP4 weight-only GEMM library
+ * (libnvfp4.so).
+ *
+ * What the library computes
+ * -------------------------
+ * NVFP4 weights: each value is an E2M1 4-bit float (1 sign, 2 exponent, 1
+ * mantissa bit), and the format scales them in two tiers, one global FP32
+ * scale per tensor and one FP8-E4M3 scale per block of 16 consecutive values
+ * along K ("The Blackwell Architectural Split: NVFP4, Attention, and Consumer
+ * Silicon", section "Preserving precision -- dual-tier scale handling"; the
+ * A4Q section of the same page dequantizes exactly such 16-value blocks).
+ * Activations and outputs are BF16 ("The SM120 FP4 GEMM Kernel
+ * Investigation", section "The Context": 4-bit weights with BF16
+ * activations).  The grouped GEMM runs every expert of a MoE layer in one
+ * launch over per-expert token segments ("The FP4 Frontier", Finding 5:
+ * grouped GEMM over all experts in a persistent kernel).
+ *
+ * Encoding (nvfp4_quantize), for one tensor W [n][k] in BF16:
+ *   g      = fl32(amax(|W|) / 2688)                 (2688 = 6 * 448)
+ *   s[b]   = E4M3_rne_sat(fl32(fl32(amax_b / 6) / g)), or 0 when g == 0
+ *   d      = fl32(decode(s[b]) * g)
+ *   code   = sign(w) << 3 | E2M1_rne_sat(fl32(|w| / d))   (magnitude 0 if d == 0)
+ * "rne_sat": round to nearest, ties to the even code, clamp to the largest
+ * finite value (448, resp. 6).  The sign bit is kept for values that round to
+ * zero, so -0 encodes as 0x8.
+ *
+ * Product (nvfp4_gemm, nvfp4_grouped_gemm):
+ *   y[m][n] = g * sum_k x[m][k] * e2m1(code[n][k]) * decode(s[n][k/16])
+ * Each e2m1 * E4M3 product is exact in BF16, so the kernels run BF16 MFMA with
+ * FP32 accumulation and apply g once in the epilogue; the BF16 output is the
+ * round-to-nearest-even of fl32(g * acc).
+ *
+ * Memory layout (all row-major, contiguous, device memory)
+ * ---------------------------------------------------------
+ *   W       bf16   [batch][n][k]
+ *   packed  uint8  [batch][n][k/2]   byte j of a row: element 2j in the low
+ *                                     nibble, element 2j+1 in the high nibble
+ *   scales  uint8  [batch][n][k/16]  E4M3 (OCP "FN": max 448, no infinities)
+ *   g       float  [batch]
+ *   x       bf16   [m][k]            grouped: [rows][k], sorted by expert
+ *   y       bf16 or float [m][n]     grouped: [rows][n]
+ * Storage is exactly 4.5 bits per weight plus 32 bits per tensor ("The FP4
+ * Frontier", Finding 6).
+ *
+ * Conventions
+ * -----------
+ *  - Ownership: the caller owns every buffer.  The library allocates no
+ *    device or host memory; the only state it keeps is cached device
+ *    properties (compute-unit count) per device.
+ *  - Pointers are device pointers unless stated otherwise; `stream` is a
+ *    hipStream_t (NULL means the default stream).  Every call only enqueues
+ *    work on `stream` and returns without waiting for it.
+ *  - Alignment: x, y, W, packed, scales and workspace must be 16-byte aligned,
+ *    else NVFP4_ERR_MISALIGNED.  k must be a positive multiple of 16.  Any
+ *    n >= 1, m >= 0 and k % 16 == 0 is supported; k % 64 == 0 takes the fast
+ *    path.  m == 0 (or rows == 0) is a no-op that returns NVFP4_OK.
+ *  - Errors the host can check are returned synchronously and nothing is
+ *    enqueued.  A launch failure is returned as NVFP4_ERR_HIP.  No call ever
+ *    "succeeds" without writing its outputs: an unsupported combination
+ *    returns NVFP4_ERR_UNSUPPORTED.
+ *  - Data-dependent errors set bits in the caller-provided device word
+ *    `d_status` (may be NULL): NVFP4_DSTATUS_NONFINITE (quantize saw a NaN
+ *    or infinity; outputs for that tensor are unspecified) and
+ *    NVFP4_DSTATUS_BAD_OFFSETS (grouped GEMM saw offsets that are not a
+ *    non-decreasing prefix array from 0 to rows; nothing is written to y).
+ *    Bits are only ever set (atomic OR), never cleared, by the library.
+ *  - Workspace: a device buffer of at least the size the matching
+ *    *_workspace_size() function returns (0: pass NULL).  For the two GEMM
+ *    calls, the first nvfp4_workspace_counter_bytes() bytes of a non-empty
+ *    workspace hold split-K tile counters that must be zero before the first
+ *    call that uses the buffer (nvfp4_workspace_init zeroes them); every
+ *    completed call leaves them zero again.  The quantize workspace has no
+ *    counters and needs no initialization.  Calls that may run concurrently
+ *    need separate workspaces.
+ */
+#ifndef NVFP4_H_
+#define NVFP4_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NVFP4_OK = 0,
+  NVFP4_ERR_INVALID_ARGUMENT = 1, /* bad size, null pointer, k % 16 != 0 */
+  NVFP4_ERR_MISALIGNED = 2,       /* a buffer is not 16-byte aligned */
+  NVFP4_ERR_UNSUPPORTED = 3,      /* valid but not implemented (e.g. > 1024 experts) */
+  NVFP4_ERR_WORKSPACE = 4,        /* workspace missing or too small */
+  NVFP4_ERR_HIP = 5               /* the HIP runtime reported an error */
+} nvfp4_status_t;
+
+typedef enum { NVFP4_OUT_BF16 = 0, NVFP4_OUT_F32 = 1 } nvfp4_out_t;
+
+#define NVFP4_DSTATUS_NONFINITE 1u
+#define NVFP4_DSTATUS_BAD_OFFSETS 2u
+
+/* Largest number of experts nvfp4_grouped_gemm accepts. */
+#define NVFP4_MAX_EXPERTS 1024
+
+/* Encode `batch` BF16 tensors W [batch][n][k] (two passes over W: tensor
+ * amax, then block scales, element codes and nibble packing).  Writes
+ * packed [batch][n][k/2], scales [batch][n][k/16] and global_scale [batch]
+ * (device).  The encoding is bit-exact with the definition above: IEEE
+ * binary32 division, no flush of subnormals.  Non-finite input sets
+ * NVFP4_DSTATUS_NONFINITE in *d_status. */
+nvfp4_status_t nvfp4_quantize(const void* w_bf16, int64_t batch, int64_t n, int64_t k,
+                              uint8_t* packed, uint8_t* scales, float* global_scale,
+                              uint32_t* d_status, void* workspace, size_t ws_bytes,
+                              void* stream);
+
+/* Dense W4A16 GEMM: y [m][n] = x [m][k] (bf16) times the decoded weight
+ * (packed, scales, *global_scale -- a device pointer to one float).  The
+ * schedule (rows per tile, split of K over workgroups for m <= 64) is chosen
+ * from the shape and the device's compute-unit count; split-K partial sums
+ * are reduced in a fixed order, so results are bitwise reproducible. */
+nvfp4_status_t nvfp4_gemm(const void* x_bf16, int64_t m, int64_t n, int64_t k,
+                          const uint8_t* packed, const uint8_t* scales,
+                          const float* global_scale, void* y, nvfp4_out_t out,
+                          void* workspace, size_t ws_bytes, void* stream);
+
+/* Grouped (MoE) W4A16 GEMM.  x [rows][k] holds the routed token rows sorted
+ * by expert; expert_offsets (device, int32 [num_experts + 1]) is the prefix
+ * array: rows [offsets[e], offsets[e+1]) use expert e's weight
+ * packed[e] [n][k/2], scales[e] [n][k/16], global_scales[e].  Empty experts
+ * cost nothing and write nothing.  The offsets are read on the device (no
+ * host synchronization); a persistent grid walks all (expert, row tile,
+ * column tile, K split) work units.  Bad offsets set
+ * NVFP4_DSTATUS_BAD_OFFSETS in *d_status (may be NULL) and write nothing. */
+nvfp4_status_t nvfp4_grouped_gemm(const void* x_bf16, int64_t rows,
+                                  const int32_t* expert_offsets, int64_t num_experts,
+                                  int64_t n, int64_t k, const uint8_t* packed,
+                                  const uint8_t* scales, const float* global_scales,
+                                  void* y, nvfp4_out_t out, uint32_t* d_status,
+                                  void* workspace, size_t ws_bytes, void* stream);
+
+/* Workspace sizes (bytes) for the calls above; 0 means none is needed.  The
+ * sizes depend on the current device's compute-unit count. */
+size_t nvfp4_quantize_workspace_size(int64_t batch, int64_t n, int64_t k);
+size_t nvfp4_gemm_workspace_size(int64_t m, int64_t n, int64_t k);
+size_t nvfp4_grouped_gemm_workspace_size(int64_t rows, int64_t num_experts, int64_t n,
+                                         int64_t k);
+/* Bytes at the start of any workspace that hold tile counters. */
+size_t nvfp4_workspace_counter_bytes(void);
+
+/* Zero the counter region of a workspace of ws_bytes bytes on `stream` (a
+ * fill kernel, no memset node, so it may be captured in a HIP graph). */
+nvfp4_status_t nvfp4_workspace_init(void* workspace, size_t ws_bytes, void* stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* nvfp4_status_string(nvfp4_status_t status);
+
+/* Library version as MAJOR * 10000 + MINOR * 100 + PATCH. */
+int nvfp4_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NVFP4_H_ */

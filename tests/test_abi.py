@@ -1,0 +1,115 @@
+"""CPU checks of the C ABI: the library loads, exports every function that
+include/nvfp4.h declares, and rejects bad arguments on the host before
+touching the GPU (no compute calls here).  Boundary lesson: a backend that
+returned all zeros without an error ("The SM120 FP4 GEMM Kernel
+Investigation", section "The Breaking Point: FlashInfer #2577") -- every bad
+call here must return a non-OK status instead."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_scaled_fp4_nibble_amd as nv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(nv.LIB_PATH):
+        pytest.fail("libnvfp4.so is not built (run __graft_entry__.build())")
+    return nv.load_library()
+
+
+def test_header_lists_the_entry_points():
+    fns = declared_functions()
+    for f in ("nvfp4_quantize", "nvfp4_gemm", "nvfp4_grouped_gemm"):
+        assert f in fns
+    assert sorted(nv.EXPORTED) == fns
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for f in declared_functions():
+        assert hasattr(lib, f), f
+
+
+def test_exports_are_c_symbols():
+    raw = ctypes.CDLL(nv.LIB_PATH)
+    for f in declared_functions():
+        ctypes.cast(getattr(raw, f), ctypes.c_void_p)  # resolvable unmangled
+
+
+def test_status_strings(lib):
+    for code, name in nv.STATUS_NAMES.items():
+        assert nv.nvfp4_status_string(code) == name
+    assert nv.nvfp4_status_string(99) == "NVFP4_ERR_UNKNOWN"
+    assert nv.nvfp4_version() >= 100
+    assert nv.nvfp4_workspace_counter_bytes() % 16 == 0
+
+
+class FakePtr:
+    """Stands in for a tensor: only an address, never dereferenced because
+    every call below is rejected on the host."""
+
+    def __init__(self, addr):
+        self.addr = addr
+
+    def data_ptr(self):
+        return self.addr
+
+
+A = FakePtr(0x10000)        # aligned
+MIS = FakePtr(0x10008)      # 8-byte aligned only
+
+
+class FakeStream:
+    cuda_stream = 0
+
+
+S = FakeStream()
+
+
+def gemm_call(x=A, m=4, n=8, k=32, packed=A, scales=A, g=A, y=A, out=nv.OUT_BF16):
+    return nv.nvfp4_gemm(x, m, n, k, packed, scales, g, y, out, None, 0, S)
+
+
+def test_gemm_host_validation(lib):
+    assert gemm_call(k=24) == 1           # k % 16 != 0
+    assert gemm_call(k=0) == 1
+    assert gemm_call(n=0) == 1
+    assert gemm_call(m=-1) == 1
+    assert gemm_call(out=7) == 1
+    assert gemm_call(x=None) == 1
+    assert gemm_call(y=MIS) == 2          # misaligned
+    assert gemm_call(packed=MIS) == 2
+    assert gemm_call(m=0, x=None, y=None) == 0  # empty problem is a no-op
+
+
+def test_grouped_host_validation(lib):
+    def call(E=4, offsets=A, rows=8, k=32):
+        return nv.nvfp4_grouped_gemm(A, rows, offsets, E, 8, k, A, A, A, A, nv.OUT_BF16, None,
+                                     None, 0, S)
+    assert call(E=0) == 1
+    assert call(E=nv.MAX_EXPERTS + 1) == 3   # unsupported, never silent
+    assert call(offsets=None) == 1
+    assert call(offsets=FakePtr(0x10002)) == 2
+    assert call(k=40) == 1
+    assert call(rows=0, offsets=None) == 0
+
+
+def test_quantize_host_validation(lib):
+    def call(batch=1, n=4, k=32, w=A, ws=None):
+        return nv.nvfp4_quantize(w, batch, n, k, A, A, A, None, ws, 0, S)
+    assert call(k=8) == 1
+    assert call(n=0) == 1
+    assert call(batch=-1) == 1
+    assert call(w=MIS) == 2
+    assert call(batch=0) == 0

@@ -1,0 +1,198 @@
+"""GPU parity of the MoE grouped GEMM against the oracle.
+
+One persistent launch over all experts' token segments ("The FP4 Frontier",
+Finding 5), at the decode batches where the pages report utilization
+collapsing: ~16 and ~64 tokens per expert ("The FP4 Frontier", section "The
+Context").  Full-size workloads are checked on sampled outputs plus the
+property that every routed row is written; reduced sizes are checked in
+full."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_helpers import (BF16_TOL, F32_TOL, check_close, dev, host, normalized_error,
+                         output_values, require_gpu, sample_positions)
+
+pytestmark = pytest.mark.gpu
+
+
+def oracle_weights(w_bits):
+    return oracle.quantize(w_bits)
+
+
+def to_qw(nv, p, s, g):
+    return nv.QuantizedWeight(dev(p), dev(s), dev(g))
+
+
+def run_grouped(nv, x, offsets, qw, out_dtype, d_status=None):
+    rows = x.shape[0]
+    out = torch.full((rows, qw.n), float("nan"), dtype=out_dtype, device="cuda")
+    y = nv.grouped_gemm(dev(x), dev(offsets.astype(np.int32)), qw, out_dtype=out_dtype, out=out,
+                        d_status=d_status)
+    torch.cuda.synchronize()
+    return y
+
+
+def small_case(counts, n, k, seed):
+    E = len(counts)
+    off = np.zeros(E + 1, np.int32)
+    off[1:] = np.cumsum(counts)
+    x = W.normal_bf16((int(off[-1]), k), 1.0, (90, seed, 1))
+    w = W.normal_bf16((E, n, k), 0.02, (90, seed, 2))
+    return x, off, w
+
+
+@pytest.mark.parametrize("counts,n,k", [
+    ([3, 0, 17, 1, 0, 40, 64, 65], 300, 576),
+    ([16] * 8, 256, 512),
+    ([0, 0, 0, 5], 64, 48),
+    ([1], 17, 16),
+    ([100, 0, 3], 513, 1040),
+])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_small_full(counts, n, k, out_dtype):
+    nv = require_gpu()
+    x, off, w = small_case(counts, n, k, seed=sum(counts) * 7 + n + k)
+    p, s, g = oracle_weights(w)
+    y_ref, d = oracle.grouped_gemm(x, off, p, s, g)
+    y = run_grouped(nv, x, off, to_qw(nv, p, s, g), out_dtype)
+    check_close(y, y_ref, d, "grouped %s n=%d k=%d" % (counts, n, k))
+
+
+def _sampled_check(nv, x, r, p, s, g, out_dtype, seed, count=3000):
+    y = run_grouped(nv, x, r.offsets, to_qw(nv, p, s, g), out_dtype)
+    yv = output_values(y)
+    assert np.isfinite(yv).all(), "a routed row was not written"
+    rows, cols = sample_positions(r.rows, yv.shape[1], count, seed)
+    y_ref, d = oracle.grouped_gemm_sampled(x, r.offsets, p, s, g, rows, cols)
+    err = normalized_error(yv[rows, cols], y_ref, d)
+    tol = F32_TOL if out_dtype == torch.float32 else BF16_TOL
+    assert err <= tol, err
+    return y
+
+
+@pytest.fixture(scope="module")
+def moe_uniform():
+    r, x, w = W.moe_uniform_inputs()
+    p, s, g = oracle_weights(w)
+    return r, x, p, s, g
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_uniform_16_tokens_per_expert(moe_uniform, out_dtype):
+    nv = require_gpu()
+    r, x, p, s, g = moe_uniform
+    assert (r.counts == 0).sum() == 4
+    _sampled_check(nv, x, r, p, s, g, out_dtype, seed=31)
+
+
+def test_uniform_full_rows_of_two_experts(moe_uniform):
+    """Every output of the first and the largest non-empty expert in full."""
+    nv = require_gpu()
+    r, x, p, s, g = moe_uniform
+    y = output_values(run_grouped(nv, x, r.offsets, to_qw(nv, p, s, g), torch.float32))
+    for e in [int(np.nonzero(r.counts)[0][0]), int(np.argmax(r.counts))]:
+        r0, r1 = r.offsets[e], r.offsets[e + 1]
+        y_ref, d = oracle.gemm(x[r0:r1], p[e], s[e], g[e])
+        assert normalized_error(y[r0:r1], y_ref, d) <= F32_TOL
+
+
+@pytest.fixture(scope="module")
+def moe_zipf_up():
+    r, x, w = W.moe_zipf_up_inputs()
+    p, s, g = oracle_weights(w)
+    return r, x, p, s, g
+
+
+@pytest.fixture(scope="module")
+def moe_zipf_down():
+    r, h, w = W.moe_zipf_down_inputs()
+    p, s, g = oracle_weights(w)
+    return r, h, p, s, g
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_zipf_up(moe_zipf_up, out_dtype):
+    nv = require_gpu()
+    r, x, p, s, g = moe_zipf_up
+    _sampled_check(nv, x, r, p, s, g, out_dtype, seed=41)
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_zipf_down(moe_zipf_down, out_dtype):
+    nv = require_gpu()
+    r, h, p, s, g = moe_zipf_down
+    _sampled_check(nv, h, r, p, s, g, out_dtype, seed=43)
+
+
+def test_zipf_hot_expert_full(moe_zipf_up):
+    """The hottest expert (hundreds of rows, several row tiles) in full."""
+    nv = require_gpu()
+    r, x, p, s, g = moe_zipf_up
+    y = output_values(run_grouped(nv, x, r.offsets, to_qw(nv, p, s, g), torch.float32))
+    e = int(np.argmax(r.counts))
+    assert r.counts[e] > 256
+    r0, r1 = r.offsets[e], r.offsets[e + 1]
+    y_ref, d = oracle.gemm(x[r0:r1], p[e], s[e], g[e])
+    assert normalized_error(y[r0:r1], y_ref, d) <= F32_TOL
+
+
+def test_zipf_with_empty_experts():
+    nv = require_gpu()
+    r, x, w = W.moe_zipf_up_inputs(n=512, k=1024, excluded=(3, 17, 40, 63))
+    assert (r.counts == 0).sum() == 4
+    p, s, g = oracle_weights(w)
+    y_ref, d = oracle.grouped_gemm(x, r.offsets, p, s, g)
+    y = run_grouped(nv, x, r.offsets, to_qw(nv, p, s, g), torch.float32)
+    check_close(y, y_ref, d, "zipf with empties")
+
+
+def test_single_hot_expert_matches_dense():
+    nv = require_gpu()
+    x, off, w = small_case([0, 0, 48, 0], 256, 512, seed=5)
+    p, s, g = oracle_weights(w)
+    y = run_grouped(nv, x, off, to_qw(nv, p, s, g), torch.float32)
+    y_ref, d = oracle.gemm(x, p[2], s[2], g[2])
+    check_close(y, y_ref, d, "single expert")
+    yd = nv.gemm(dev(x), nv.QuantizedWeight(dev(p[2]), dev(s[2]), dev(g[2:3])),
+                 out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    check_close(yd, y_ref, d, "dense")
+
+
+@pytest.mark.parametrize("bad", ["decreasing", "first_nonzero", "last_wrong"])
+def test_bad_offsets_set_status_and_write_nothing(bad):
+    nv = require_gpu()
+    x, off, w = small_case([4, 4, 4, 4], 64, 64, seed=9)
+    p, s, g = oracle_weights(w)
+    off = off.copy()
+    if bad == "decreasing":
+        off[2] = 1
+    elif bad == "first_nonzero":
+        off[0] = 2
+    else:
+        off[-1] = 15
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    y = run_grouped(nv, x, off, to_qw(nv, p, s, g), torch.float32, d_status=status)
+    assert int(status.item()) & nv.DSTATUS_BAD_OFFSETS
+    assert np.isnan(host(y)).all()
+
+
+def test_zero_rows_is_noop():
+    nv = require_gpu()
+    x, off, w = small_case([0, 0], 64, 64, seed=11)
+    p, s, g = oracle_weights(w)
+    y = nv.grouped_gemm(dev(x), dev(off), to_qw(nv, p, s, g))
+    torch.cuda.synchronize()
+    assert y.shape == (0, 64)
+
+
+def test_reproducible(moe_uniform):
+    nv = require_gpu()
+    r, x, p, s, g = moe_uniform
+    qw = to_qw(nv, p, s, g)
+    a = host(run_grouped(nv, x, r.offsets, qw, torch.float32)).view(np.uint32)
+    b = host(run_grouped(nv, x, r.offsets, qw, torch.float32)).view(np.uint32)
+    assert np.array_equal(a, b)

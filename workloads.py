@@ -38,12 +38,10 @@ def _threads() -> int:
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """Round float32 to BF16 (nearest, ties to even); returns uint16 bits."""
-    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
-    nan = (u & 0x7FFFFFFF) > 0x7F800000
-    r = ((u.astype(np.uint64) + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
-    if nan.any():
-        r[nan] = ((u[nan] >> 16) | 0x40).astype(np.uint16)
-    return r
+    import torch  # CPU cast only
+
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
 def bf16_bits_to_f32(h: np.ndarray) -> np.ndarray:

@@ -1,0 +1,331 @@
+#!/usr/bin/env python3
+"""Benchmark: NVFP4 W4A16 MoE grouped GEMM at 16-64 tokens per expert on one
+MI355X.
+
+One step = the three grouped GEMMs that span the decode range where the pages
+report utilization collapsing ("The FP4 Frontier", section "The Context":
+15-55 TFLOPS at 16-64 tokens per expert on their hardware):
+  1. up projection, 64 experts, N=4096, K=6144, 128 tokens top-8 uniform
+     over 60 experts (~16 rows per expert, 4 experts empty);
+  2. up projection, 64 experts, N=4096, K=6144, 512 tokens top-8 with
+     Zipf(1.2) expert skew (~64 rows per expert on average);
+  3. down projection of the same routing, N=6144, K=2048.
+Weights are NVFP4 (encoded once by nvfp4_quantize before timing, as a model
+load would); activations and outputs BF16; all inputs are resident in HBM
+when the timed region starts.  Each launch streams more weight bytes (0.45 to
+0.91 GB) than the 256 MB Infinity Cache holds, so weights come from HBM.
+
+Output: one JSON line.  value = useful TFLOPS of the step (2 * rows * N * K
+summed over the three launches, divided by wall time of the timed steps);
+roofline = algorithmic HBM bytes per launch of the dominant kernel over its
+average launch time (HIP events on the launch stream), against 8 TB/s;
+cpu_baseline = the CPU oracle timed on a bounded sample of launch 1.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "TFLOPS + HBM GB/s (% roofline), NVFP4 grouped GEMM at 16-64 tok/expert"
+HBM_PEAK_GBPS = 8000.0
+BF16_DENSE_PEAK_TFLOPS = 2500.0
+KERNEL_SOURCE = os.path.join(ROOT, "block_scaled_fp4_nibble_amd", "csrc", "gemm.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the dense decode / 8192^3 / quantize side measurements")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum CPU time spent on the oracle sample")
+    return ap.parse_args()
+
+
+def grouped_bytes(counts, n, k):
+    """Algorithmic HBM bytes of one grouped launch: each non-empty expert's
+    packed weight + scales + global scale once, activations read once, output
+    written once, offsets read once."""
+    nonempty = sum(1 for c in counts if c > 0)
+    rows = int(sum(counts))
+    return nonempty * (n * k * 9 // 16 + 4) + 2 * rows * k + 2 * rows * n + 4 * (len(counts) + 1)
+
+
+def dense_bytes(m, n, k):
+    return n * k * 9 // 16 + 4 + 2 * m * k + 2 * m * n
+
+
+def randn_bf16(shape, std, seed, device="cuda"):
+    """Seeded N(0, std^2) BF16 tensor drawn on the GPU (torch's generator)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    t = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    if std != 1.0:
+        t.mul_(std)
+    return t.to(torch.bfloat16)
+
+
+def build_workload():
+    import numpy as np
+    import torch
+    import block_scaled_fp4_nibble_amd as nv
+    import workloads as W
+
+    launches = []
+    specs = [
+        ("up_uniform_16tpe", W.moe_uniform_routing(), 4096, 6144, 101),
+        ("up_zipf_64tpe", W.moe_zipf_routing(), 4096, 6144, 102),
+        ("down_zipf_64tpe", W.moe_zipf_routing(), 6144, 2048, 103),
+    ]
+    for name, r, n, k, seed in specs:
+        E = r.num_experts
+        w = randn_bf16((E, n, k), 0.02, seed)
+        qw = nv.quantize(w)
+        del w
+        x = randn_bf16((r.rows, k), 1.0, seed + 1000)
+        off = torch.from_numpy(r.offsets.astype(np.int32)).cuda()
+        y = torch.empty((r.rows, n), dtype=torch.bfloat16, device="cuda")
+        launches.append(dict(name=name, qw=qw, x=x, off=off, y=y, n=n, k=k, rows=r.rows,
+                             counts=r.counts.tolist(), experts=E,
+                             bm=bm_for(r.rows, E),
+                             flops=2 * r.rows * n * k, bytes=grouped_bytes(r.counts, n, k)))
+    torch.cuda.synchronize()
+    return launches
+
+
+def bm_for(rows, experts):
+    # mirrors the library's row-tile choice for grouped launches (for naming
+    # the kernel instantiation in the roofline record)
+    avg = (rows + experts - 1) // experts
+    bm = 16 if avg <= 16 else (32 if avg <= 32 else 64)
+    if 8 < avg <= 24:
+        bm = 32
+    return bm
+
+
+def run_launch(L):
+    import block_scaled_fp4_nibble_amd as nv
+    nv.grouped_gemm(L["x"], L["off"], L["qw"], out=L["y"])
+
+
+def traffic_record(kernel_name):
+    """HBM traffic measured with rocprofv3 counters, if the record matches the
+    current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    ent = rec.get(kernel_name)
+    if not ent or ent.get("source_sha256") != sha:
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(min_seconds):
+    """The CPU oracle (plain C, OpenMP over rows) on whole expert segments of
+    launch 1 until at least `min_seconds` of wall time have been spent."""
+    import numpy as np
+    import oracle
+    import workloads as W
+
+    r = W.moe_uniform_routing()
+    n, k = 4096, 6144
+    flops = 0
+    elapsed = 0.0
+    experts = 0
+    rows = 0
+    for e in range(r.num_experts):
+        c = int(r.counts[e])
+        if c == 0:
+            continue
+        w = W.normal_bf16((1, n, k), 0.02, (W.SEED, W.W_MOE_UNIFORM, W.S_WEIGHT, 500 + e))
+        x = W.normal_bf16((c, k), 1.0, (W.SEED, W.W_MOE_UNIFORM, W.S_ACT, 500 + e))
+        p, s, g = oracle.quantize(w)
+        off = np.array([0, c], np.int32)
+        t0 = time.perf_counter()
+        oracle.grouped_gemm(x, off, p, s, g)
+        elapsed += time.perf_counter() - t0
+        flops += 2 * c * n * k
+        experts += 1
+        rows += c
+        if elapsed >= min_seconds:
+            break
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count()
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOPS", "cores": threads,
+            "kind": "oracle",
+            "sample": "%d experts (%d rows) of the ~16 tok/expert up projection "
+                      "(N=4096, K=6144), FP64-accumulate oracle GEMM, %.1f s" %
+                      (experts, rows, elapsed)}
+
+
+def time_fn(fn, iters, warm):
+    import torch
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(iters):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / iters  # ms
+
+
+def extras():
+    """Side measurements on the other workloads (not the headline value)."""
+    import torch
+    import block_scaled_fp4_nibble_amd as nv
+
+    out = {}
+    # dense decode: N=4096, K=7168; 4 weight copies rotated so each launch reads
+    # a copy not touched for 3 launches (3 x 16.5 MB, still inside the 256 MB
+    # Infinity Cache, so this is a warm-cache figure)
+    n, k = 4096, 7168
+    ws = [nv.quantize(randn_bf16((n, k), 0.02, 200 + i)) for i in range(4)]
+    for m in (1, 16, 64):
+        x = randn_bf16((m, k), 1.0, 300 + m)
+        y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+        it = [0]
+
+        def f():
+            nv.gemm(x, ws[it[0] % 4], out=y)
+            it[0] += 1
+        ms = time_fn(f, 50, 10)
+        out["dense_decode_m%d" % m] = {"us": ms * 1e3,
+                                       "GBps": dense_bytes(m, n, k) / (ms * 1e-3) / 1e9,
+                                       "TFLOPS": 2 * m * n * k / (ms * 1e-3) / 1e12}
+    del ws
+    # 8192^3 dense GEMM and the bulk quantize of its weight
+    m = n = k = 8192
+    w = randn_bf16((n, k), 0.02, 400)
+    qw = nv.quantize(w)
+    x = randn_bf16((m, k), 1.0, 401)
+    y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    ms = time_fn(lambda: nv.gemm(x, qw, out=y), 5, 2)
+    tf = 2 * m * n * k / (ms * 1e-3) / 1e12
+    out["dense_8192_cubed"] = {"ms": ms, "TFLOPS": tf,
+                               "frac_of_bf16_peak": tf / BF16_DENSE_PEAK_TFLOPS}
+    ms = time_fn(lambda: nv.quantize(w), 10, 2)
+    qbytes = 2 * (n * k * 2) + n * k * 9 // 16 + 4  # two reads of W, one write
+    out["quantize_8192x8192"] = {"us": ms * 1e3, "GBps": qbytes / (ms * 1e-3) / 1e9}
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: every box here has a single MI355X, so "
+              "--gpus %d is not supported (the sharding design is described in the docs)" %
+              args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    launches = build_workload()
+    step_flops = sum(L["flops"] for L in launches)
+    step_bytes = sum(L["bytes"] for L in launches)
+
+    for _ in range(args.warmup):
+        for L in launches:
+            run_launch(L)
+    torch.cuda.synchronize()
+
+    # timed region: per-launch HIP events on the launch stream, wall clock
+    # around the whole region with synchronization on both sides
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(launches) + 1)]
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        evs[i][0].record()
+        for j, L in enumerate(launches):
+            run_launch(L)
+            evs[i][j + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    launch_ms = [sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)) /
+                 args.steps for j in range(len(launches))]
+
+    # dominant kernel instantiation by total time
+    by_bm = {}
+    for L, ms in zip(launches, launch_ms):
+        d = by_bm.setdefault(L["bm"], {"ms": 0.0, "bytes": 0, "launches": 0, "names": []})
+        d["ms"] += ms
+        d["bytes"] += L["bytes"]
+        d["launches"] += 1
+        d["names"].append(L["name"])
+    bm, dom = max(by_bm.items(), key=lambda kv: kv[1]["ms"])
+    kernel = "nvfp4::gemm_kernel<%d, true>" % bm
+    avg_ms = dom["ms"] / dom["launches"]
+    bytes_per_launch = dom["bytes"] / dom["launches"]
+    achieved = bytes_per_launch / (avg_ms * 1e-3) / 1e9
+    tr = traffic_record(kernel)
+
+    result = {
+        "metric": METRIC,
+        "value": step_flops / (ms_per_step * 1e-3) / 1e12,
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "moe_grouped_gemm_16_to_64_tok_per_expert",
+            "experts": 64,
+            "launches": [{"name": L["name"], "rows": L["rows"], "n": L["n"], "k": L["k"],
+                          "nonempty_experts": sum(1 for c in L["counts"] if c),
+                          "max_rows_per_expert": max(L["counts"]),
+                          "us": ms * 1e3,
+                          "TFLOPS": L["flops"] / (ms * 1e-3) / 1e12,
+                          "GBps": L["bytes"] / (ms * 1e-3) / 1e9}
+                         for L, ms in zip(launches, launch_ms)],
+        },
+        "hbm_gbps": step_bytes / (ms_per_step * 1e-3) / 1e9,
+        "hbm_frac": step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": kernel,
+            "launches": dom["names"],
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "avg_launch_us": avg_ms * 1e3,
+            "algorithmic_bytes_per_launch": bytes_per_launch,
+            "traffic": tr,
+        },
+    }
+    if not args.no_extras:
+        result["extras"] = extras()
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

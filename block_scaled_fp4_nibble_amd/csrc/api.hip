@@ -116,6 +116,8 @@ static nvfp4_status_t check_gemm_common(const void* x, int64_t rows, int64_t n, 
   if (rows < 0 || n < 1 || check_k(k) != NVFP4_OK) return NVFP4_ERR_INVALID_ARGUMENT;
   if (out != NVFP4_OUT_BF16 && out != NVFP4_OUT_F32) return NVFP4_ERR_INVALID_ARGUMENT;
   if (rows >= kInt31 || n >= kInt31) return NVFP4_ERR_UNSUPPORTED;
+  // per-expert weight bytes are addressed with 32-bit buffer offsets
+  if (n * (k / 2) >= kInt31 || k >= ((int64_t)1 << 24)) return NVFP4_ERR_UNSUPPORTED;
   if (rows == 0) return NVFP4_OK;
   if (!x || !packed || !scales || !g || !y) return NVFP4_ERR_INVALID_ARGUMENT;
   if (!aligned16(x) || !aligned16(packed) || !aligned16(scales) || !aligned16(y) ||

@@ -11,9 +11,10 @@
 // experts with smaller tiles and adaptive grids for small batches (same page,
 // Finding 5).  Dequantization happens in registers, 16 values per scale, just
 // before the matrix instruction -- the register-level idea of the A4Q section
-// of the first page -- instead of staging unpacked weights in shared memory,
-// which is what overflowed shared memory on the pages' hardware ("The
-// Problem Shared Memory Brick Wall" on the same page).
+// of the first page.  Unpacked weights are never staged in shared memory
+// (staging them was what overflowed it on the pages' hardware, section "The
+// Problem Shared Memory Brick Wall" of the same page); only the packed
+// 4.5-bit data passes through LDS.
 //
 // gfx950 design
 //  - One persistent grid.  A work unit is (expert, row tile of BM rows,
@@ -21,22 +22,27 @@
 //    expert offsets from device memory, builds the per-expert unit prefix in
 //    LDS and walks units blockIdx.x, +gridDim.x, ...  Empty experts own no
 //    units.  There is no host synchronization and no inter-workgroup wait.
-//  - 4 waves per workgroup; each wave owns 64 weight rows = 4 MFMA column
-//    tiles.  Lane l of a wave covers weight row (l % 16) of each tile and the
-//    64-wide K range 64*(l/16) of every 256-wide K chunk: two 16-byte loads of
-//    packed nibbles and one 4-byte load of its four block scales.  Each weight
-//    byte is loaded from HBM once per row tile.
-//  - MFMA v_mfma_f32_16x16x32_bf16.  Its 32 K slots are assigned so that lane
-//    group q = l/16 supplies K = kc + 64q + 8i .. +7 in step i (i = 0..7) for
-//    both operands; the order of a sum does not change its exact value, and
-//    the assignment keeps every lane's weight bytes contiguous.
-//  - Activations: a BM x 256 BF16 chunk is staged in LDS (rows padded by
-//    16 bytes so the 16-byte fragment reads of 16 rows hit distinct banks)
-//    and shared by the 4 waves.
+//  - MFMA v_mfma_f32_16x16x32_bf16.  Operand A = activations (16 rows),
+//    operand B = dequantized weights (16 weight rows = 16 output columns).
+//    Lane l holds row/column l % 16 and 8 consecutive K of lane group
+//    q = l / 16; which real K a slot carries is a free choice as long as A and
+//    B agree, and it is chosen so that each lane's weight bytes are
+//    contiguous.
 //  - Dequant: a nibble pair becomes two exact FP32 values with the gfx950 FP4
-//    conversion, is multiplied by the decoded E4M3 scale (exact), and the
+//    conversion (scale 1.0; the instruction would apply only the exponent of
+//    a scale), is multiplied by the decoded E4M3 block scale (exact), and the
 //    upper halves form two BF16 values.  The global scale g is applied once
 //    to the FP32 accumulator in the epilogue.
+//  - Ring kernel (k % 64 == 0): 8 waves, each owning 32 of the 256 columns.
+//    K advances in 128-wide stages held in a 4-deep LDS ring: packed weights
+//    (256 rows x 64 B), block scales (256 x 8 B) and the activation tile
+//    (BM x 256 B), all written by buffer_load ... lds (no register staging),
+//    three stages in flight while the fourth is multiplied out.  Rows of the
+//    staged tiles are XOR-swizzled in 16-byte units so the 16-byte fragment
+//    reads of 16 lanes spread over all LDS bank groups.
+//  - Register kernel (any k % 16 == 0): 4 waves x 64 columns, weights loaded
+//    straight into registers one 256-wide chunk ahead, activations staged
+//    through a double-buffered LDS tile.
 //  - Split-K (used when there are too few output tiles to fill the chip):
 //    each split writes its FP32 partial tile to the workspace, bumps the
 //    tile's counter, and the last arrival sums the partials in split order
@@ -49,10 +55,57 @@
 
 namespace nvfp4 {
 
-constexpr int kNW = 4;                 // MFMA column tiles per wave
-constexpr int kLdsStride = kKC + 8;    // BF16 elements per staged activation row
+// ---- shared pieces ----------------------------------------------------------
 
-// Exclusive scan of one int per thread over the workgroup (256 threads).
+// Buffer resource over [base, base + bytes) for raw (stride 0) buffer loads:
+// offsets at or beyond `bytes` read as zero, which masks rows past the end.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+constexpr uint32_t kOffNone = 0x80000000u;  // beyond every resource: loads return 0
+
+// Direct global -> LDS loads (buffer_load ... lds): lane l writes its bytes
+// at M0 + l * size.  They are issued from inline assembly so that the
+// compiler does not treat every later LDS read as a possible alias of an
+// in-flight load and wait for all of them (which would serialize the ring);
+// the ring waits for exactly the stages it needs with explicit vmcnt waits.
+// M0 is saved and restored around each load.
+__device__ __forceinline__ u32x4_t rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4_t{(uint32_t)a, (uint32_t)(a >> 32), bytes, 0x00020000u};
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)(p);
+}
+
+__device__ __forceinline__ void lds_dma16(uint32_t lds, uint32_t voff, u32x4_t rsrc) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc)
+      : "memory");
+}
+
+__device__ __forceinline__ void lds_dma4(uint32_t lds, uint32_t voff, u32x4_t rsrc) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "buffer_load_dword %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc)
+      : "memory");
+}
+
+// Exclusive scan of one int per thread over a workgroup of THREADS threads.
+template <int THREADS>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int incl = v;
@@ -65,7 +118,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total)
   __syncthreads();
   int base = 0, sum = 0;
 #pragma unroll
-  for (int w = 0; w < kGemmThreads / kWave; ++w) {
+  for (int w = 0; w < THREADS / kWave; ++w) {
     base += (w < wave) ? tmp[w] : 0;
     sum += tmp[w];
   }
@@ -74,90 +127,425 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total)
   return base + incl - v;
 }
 
-template <int BM, bool FAST>
-__global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmParams p) {
-  constexpr int NF = BM / 16;  // MFMA row fragments
-  __shared__ __attribute__((aligned(16))) uint16_t xs[BM * kLdsStride];
-  __shared__ int s_off[kMaxExperts + 1];
-  __shared__ int s_units[kMaxExperts + 1];
-  __shared__ int s_tiles[kMaxExperts + 1];
-  __shared__ int s_tmp[kGemmThreads / kWave];
-  __shared__ int s_flag;
+// Per-workgroup schedule: expert segments and exclusive prefixes of work
+// units and output tiles per expert.
+struct Sched {
+  int off[kMaxExperts + 1];
+  int units[kMaxExperts + 1];
+  int tiles[kMaxExperts + 1];
+  int tmp[16];
+  int flag;
+};
 
+// Fills `sc`; returns the total unit count, or -1 (after flagging the status
+// word) when the offsets are malformed.
+template <int THREADS, int BM>
+__device__ int build_schedule(Sched& sc, const GemmParams& p) {
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int q = lane >> 4;      // lane group: K sub-range of the chunk
-  const int r16 = lane & 15;    // row within an MFMA tile
   const int E = p.num_experts;
-  const int N = p.n;
-  const int K = p.k;
-  const int S = p.splits;
-
-  // ---- expert segments and the unit prefix --------------------------------
-  for (int e = tid; e <= E; e += kGemmThreads)
-    s_off[e] = p.offsets ? p.offsets[e] : (e == 0 ? 0 : (int)p.rows);
+  for (int e = tid; e <= E; e += THREADS)
+    sc.off[e] = p.offsets ? p.offsets[e] : (e == 0 ? 0 : (int)p.rows);
   __syncthreads();
   int bad = 0;
-  for (int e = tid; e < E; e += kGemmThreads) bad |= (s_off[e + 1] < s_off[e]);
-  if (tid == 0) bad |= (s_off[0] != 0) | ((int64_t)s_off[E] != p.rows);
+  for (int e = tid; e < E; e += THREADS) bad |= (sc.off[e + 1] < sc.off[e]);
+  if (tid == 0) bad |= (sc.off[0] != 0) | ((int64_t)sc.off[E] != p.rows);
   bad = __syncthreads_or(bad);
   if (bad) {
     if (blockIdx.x == 0 && tid == 0 && p.d_status != nullptr)
       atomicOr(p.d_status, NVFP4_DSTATUS_BAD_OFFSETS);
-    return;
+    return -1;
   }
-  // each thread owns experts [4*tid, 4*tid+4)
+  constexpr int PER = (kMaxExperts + THREADS - 1) / THREADS;  // experts per thread
   int my_units = 0, my_tiles = 0;
-  for (int e = 4 * tid; e < 4 * tid + 4 && e < E; ++e) {
-    const int mt = (s_off[e + 1] - s_off[e] + BM - 1) / BM;
+  for (int e = PER * tid; e < PER * tid + PER && e < E; ++e) {
+    const int mt = (sc.off[e + 1] - sc.off[e] + BM - 1) / BM;
     my_tiles += mt * p.n_tiles;
-    my_units += mt * p.n_tiles * S;
+    my_units += mt * p.n_tiles * p.splits;
   }
   int total_units, total_tiles;
-  int ubase = block_exclusive_scan(my_units, s_tmp, &total_units);
-  int tbase = block_exclusive_scan(my_tiles, s_tmp, &total_tiles);
-  for (int e = 4 * tid; e < 4 * tid + 4 && e < E; ++e) {
-    s_units[e] = ubase;
-    s_tiles[e] = tbase;
-    const int mt = (s_off[e + 1] - s_off[e] + BM - 1) / BM;
-    ubase += mt * p.n_tiles * S;
+  int ubase = block_exclusive_scan<THREADS>(my_units, sc.tmp, &total_units);
+  int tbase = block_exclusive_scan<THREADS>(my_tiles, sc.tmp, &total_tiles);
+  for (int e = PER * tid; e < PER * tid + PER && e < E; ++e) {
+    sc.units[e] = ubase;
+    sc.tiles[e] = tbase;
+    const int mt = (sc.off[e + 1] - sc.off[e] + BM - 1) / BM;
+    ubase += mt * p.n_tiles * p.splits;
     tbase += mt * p.n_tiles;
   }
   if (tid == 0) {
-    s_units[E] = total_units;
-    s_tiles[E] = total_tiles;
+    sc.units[E] = total_units;
+    sc.tiles[E] = total_tiles;
   }
   __syncthreads();
+  return total_units;
+}
 
-  // ---- persistent loop over work units ------------------------------------
-  for (int unit = blockIdx.x; unit < total_units; unit += gridDim.x) {
-    // expert: last e with s_units[e] <= unit (empty experts have equal bounds)
-    int lo = 0, hi = E;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (s_units[mid] <= unit) lo = mid; else hi = mid;
+struct Unit {
+  int e, ks, nt, tile, row0, row_end, k_beg, k_end;
+};
+
+template <int BM>
+__device__ __forceinline__ Unit decode_unit(const Sched& sc, const GemmParams& p, int unit) {
+  // expert: last e with units[e] <= unit (empty experts have equal bounds)
+  int lo = 0, hi = p.num_experts;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (sc.units[mid] <= unit) lo = mid; else hi = mid;
+  }
+  Unit u;
+  u.e = lo;
+  const int seg0 = sc.off[lo], seg1 = sc.off[lo + 1];
+  const int mtiles = (seg1 - seg0 + BM - 1) / BM;
+  const int local = unit - sc.units[lo];
+  const int mt = local % mtiles;
+  const int rest = local / mtiles;
+  u.ks = rest % p.splits;
+  u.nt = rest / p.splits;
+  u.tile = sc.tiles[lo] + u.nt * mtiles + mt;
+  u.row0 = seg0 + mt * BM;
+  u.row_end = min(u.row0 + BM, seg1);
+  u.k_beg = u.ks * p.k_split;
+  u.k_end = min(p.k, u.k_beg + p.k_split);
+  return u;
+}
+
+// Split-K hand-off and epilogue for a workgroup of WAVES waves, each holding
+// NF x NW MFMA accumulator tiles (column = nt*256 + wave*NW*16 + j*16 + l%16,
+// row = row0 + f*16 + 4*(l/16) + r).  Returns false when another split of
+// the tile will finish it.
+template <int NF, int NW, int WAVES>
+__device__ __forceinline__ bool finish_tile(f32x4_t (&acc)[NF][NW], const GemmParams& p,
+                                            const Unit& u, Sched& sc) {
+  constexpr int BM = NF * 16;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int S = p.splits;
+  if (S > 1) {
+    float* part = p.partials + (int64_t)u.tile * S * (BM * kBN);
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int j = 0; j < NW; ++j)
+        *reinterpret_cast<f32x4_t*>(part + (int64_t)u.ks * (BM * kBN) +
+                                    (((wave * NF + f) * NW + j) * kWave + lane) * 4) = acc[f][j];
+    fence_release_agent();
+    __syncthreads();
+    if (tid == 0) {
+      const uint32_t old = atomicAdd(&p.counters[u.tile], 1u);
+      sc.flag = (old == (uint32_t)(S - 1));
     }
-    const int e = lo;
-    const int seg0 = s_off[e], seg1 = s_off[e + 1];
-    const int mtiles = (seg1 - seg0 + BM - 1) / BM;
-    const int local = unit - s_units[e];
-    const int mt = local % mtiles;
-    const int rest = local / mtiles;
-    const int ks = rest % S;
-    const int nt = rest / S;
-    const int tile = s_tiles[e] + nt * mtiles + mt;
-    const int row0 = seg0 + mt * BM;
-    const int row_end = min(row0 + BM, seg1);
-    const int k_beg = ks * p.k_split;
-    const int k_end = min(K, k_beg + p.k_split);
+    __syncthreads();
+    if (!sc.flag) return false;
+    fence_acquire_agent();
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int j = 0; j < NW; ++j) {
+        f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < S; ++s) {
+          f32x4_t v = (s == u.ks) ? acc[f][j]
+                                  : __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(
+                                        part + (int64_t)s * (BM * kBN) +
+                                        (((wave * NF + f) * NW + j) * kWave + lane) * 4));
+          sum = (s == 0) ? v : sum + v;
+        }
+        acc[f][j] = sum;
+      }
+    if (tid == 0) p.counters[u.tile] = 0u;
+  }
+  const float gv = p.g[u.e];
+  const int q = lane >> 4, r16 = lane & 15;
+#pragma unroll
+  for (int f = 0; f < NF; ++f)
+#pragma unroll
+    for (int j = 0; j < NW; ++j) {
+      const int col = u.nt * kBN + wave * (NW * 16) + j * 16 + r16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = u.row0 + f * 16 + 4 * q + r;
+        if (row < u.row_end && col < p.n) {
+          const float v = gv * acc[f][j][r];
+          if (p.out_f32)
+            reinterpret_cast<float*>(p.y)[(int64_t)row * p.n + col] = v;
+          else
+            reinterpret_cast<uint16_t*>(p.y)[(int64_t)row * p.n + col] =
+                (uint16_t)float_to_bf16_rne(v);
+        }
+      }
+    }
+  return true;
+}
 
-    const uint8_t* __restrict__ We = p.w + (int64_t)e * N * (K / 2);
-    const uint8_t* __restrict__ Se = p.s + (int64_t)e * N * (K / 16);
+// ---- ring kernel (k % 64 == 0) ------------------------------------------------
 
+constexpr int kRingThreads = 512;  // 8 waves
+constexpr int kRingWaves = kRingThreads / kWave;
+constexpr int kRingNW = 2;         // MFMA column tiles per wave
+constexpr int kRingKC = 128;       // K per stage
+constexpr int kRingStages = 4;
+
+template <int BM>
+struct RingLayout {
+  static constexpr int kW = 0;                      // 256 rows x 64 B packed nibbles
+  static constexpr int kS = kW + kBN * 64;          // 256 rows x 8 scale bytes
+  static constexpr int kX = kS + kBN * 8;           // BM rows x 256 B activations
+  static constexpr int kStage = kX + BM * 256;
+  static constexpr int kXInstr = BM / 4;            // 1 KB (4-row) loads per stage
+  static constexpr int kXPerWave = kXInstr >= kRingWaves ? kXInstr / kRingWaves : 1;
+  static constexpr int kLoadsPerWave = 2 + 1 + kXPerWave;
+};
+
+__device__ __forceinline__ void wait_vmcnt_stages(int stages_after, int per_stage) {
+  // s_waitcnt vmcnt(stages_after * per_stage): the immediate must be a
+  // constant, so the possible counts are spelled out.  Encoding (gfx9):
+  // vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt and lgkmcnt
+  // left at their maxima (no wait on them).
+#define NVFP4_VMCNT(n) \
+  __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+  const int n = stages_after * per_stage;
+  if (n == 4) NVFP4_VMCNT(4);
+  else if (n == 5) NVFP4_VMCNT(5);
+  else if (n == 8) NVFP4_VMCNT(8);
+  else if (n == 10) NVFP4_VMCNT(10);
+  else NVFP4_VMCNT(0);
+#undef NVFP4_VMCNT
+}
+
+// Issue the loads of one stage (K range [kc, kc + 128) of the unit) into LDS.
+template <int BM>
+__device__ __forceinline__ void ring_issue(uint32_t stage, u32x4_t rw, u32x4_t rs, u32x4_t rx,
+                                           int n0, int K, int kc, int k_end, int wave, int lane) {
+  using L = RingLayout<BM>;
+  // packed weights: 16 loads of 1 KB = 16 rows x 64 B; lane -> (row, slot),
+  // slot s of row R holds the row's 16-byte piece s ^ ((R >> 1) & 3)
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const int t = wave * 2 + tt;
+    const int R = t * 16 + (lane >> 2);
+    const int g = (lane & 3) ^ ((R >> 1) & 3);
+    const int kp = kc + 32 * g;
+    const uint32_t off = kp < k_end ? (uint32_t)(n0 + R) * (uint32_t)(K / 2) + (uint32_t)(kp / 2)
+                                    : kOffNone;
+    lds_dma16(stage + L::kW + t * 1024, off, rw);
+  }
+  // block scales: 8 loads of 256 B = 32 rows x 8 B, 4 bytes (4 blocks) per lane
+  {
+    const int R = wave * 32 + (lane >> 1);
+    const int kb = kc + 64 * (lane & 1);
+    const uint32_t off = kb < k_end ? (uint32_t)(n0 + R) * (uint32_t)(K / 16) + (uint32_t)(kb / 16)
+                                    : kOffNone;
+    lds_dma4(stage + L::kS + wave * 256, off, rs);
+  }
+  // activations: BM/4 loads of 1 KB = 4 rows x 256 B; slot s of row r holds
+  // piece s ^ (r & 7).  With fewer loads than waves, waves repeat a load
+  // (same bytes to the same place) so every wave issues the same count.
+#pragma unroll
+  for (int tt = 0; tt < L::kXPerWave; ++tt) {
+    const int t = L::kXInstr >= kRingWaves ? wave * L::kXPerWave + tt : wave % L::kXInstr;
+    const int r = t * 4 + (lane >> 4);
+    const int g = (lane & 15) ^ (r & 7);
+    const int kk = kc + 8 * g;
+    const uint32_t off = kk < k_end ? (uint32_t)r * (uint32_t)(K * 2) + (uint32_t)(kk * 2)
+                                    : kOffNone;
+    lds_dma16(stage + L::kX + t * 1024, off, rx);
+  }
+}
+
+// Multiply out one staged 128-wide K range: 4 MFMA steps of 32 K slots.
+// Lane group q supplies K = kc + 32q + 8i .. +7 in step i.
+template <int BM>
+__device__ __forceinline__ void ring_compute(f32x4_t (&acc)[BM / 16][kRingNW],
+                                             const uint8_t* stage, int wave, int lane) {
+  using L = RingLayout<BM>;
+  constexpr int NF = BM / 16;
+  const int q = lane >> 4, r16 = lane & 15;
+  u32x4_t wd[kRingNW];
+  float scl[kRingNW][2];
+#pragma unroll
+  for (int j = 0; j < kRingNW; ++j) {
+    const int R = wave * (kRingNW * 16) + j * 16 + r16;
+    wd[j] = *reinterpret_cast<const u32x4_t*>(stage + L::kW + R * 64 + 16 * (q ^ ((R >> 1) & 3)));
+    const uint32_t s2 = *reinterpret_cast<const uint16_t*>(stage + L::kS + R * 8 + 2 * q);
+    scl[j][0] = decode_e4m3<0>(s2);
+    scl[j][1] = decode_e4m3<1>(s2);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    bf16x8_t a[NF];
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+      a[f] = *reinterpret_cast<const bf16x8_t*>(stage + L::kX + (f * 16 + r16) * 256 +
+                                                16 * ((4 * q + i) ^ (r16 & 7)));
+#pragma unroll
+    for (int j = 0; j < kRingNW; ++j) {
+      const bf16x8_t b = dequant8(wd[j][i], scl[j][i >> 1]);
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+        acc[f][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[f], b, acc[f][j], 0, 0, 0);
+    }
+  }
+}
+
+template <int BM>
+__global__ __launch_bounds__(kRingThreads) void gemm_ring_kernel(GemmParams p) {
+  using L = RingLayout<BM>;
+  constexpr int NF = BM / 16;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kRingStages * L::kStage];
+  __shared__ Sched sc;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int total = build_schedule<kRingThreads, BM>(sc, p);
+  const int N = p.n, K = p.k;
+
+  for (int unit = blockIdx.x; unit < total; unit += gridDim.x) {
+    const Unit u = decode_unit<BM>(sc, p, unit);
+    const int n0 = u.nt * kBN;
+    const u32x4_t rw =
+        rsrc_words(p.w + (int64_t)u.e * N * (K / 2), (uint32_t)N * (uint32_t)(K / 2));
+    const u32x4_t rs =
+        rsrc_words(p.s + (int64_t)u.e * N * (K / 16), (uint32_t)N * (uint32_t)(K / 16));
+    const u32x4_t rx =
+        rsrc_words(p.x + (int64_t)u.row0 * K, (uint32_t)(u.row_end - u.row0) * (uint32_t)(K * 2));
+    const uint32_t ring0 = lds_addr(ring);
+
+    f32x4_t acc[NF][kRingNW];
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int j = 0; j < kRingNW; ++j) acc[f][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    const int nch = (u.k_end - u.k_beg + kRingKC - 1) / kRingKC;
+    for (int s = 0; s < kRingStages - 1 && s < nch; ++s)
+      ring_issue<BM>(ring0 + s * L::kStage, rw, rs, rx, n0, K, u.k_beg + s * kRingKC, u.k_end,
+                     wave, lane);
+    for (int c = 0; c < nch; ++c) {
+      // this wave's loads for stage c have landed once at most the loads of
+      // the (up to two) later stages are outstanding; the barrier extends
+      // that to every wave's loads and retires everyone's reads of stage c-1
+      wait_vmcnt_stages(min(kRingStages - 2, nch - 1 - c), L::kLoadsPerWave);
+      __syncthreads();
+      if (c + kRingStages - 1 < nch)
+        ring_issue<BM>(ring0 + ((c + kRingStages - 1) % kRingStages) * L::kStage, rw, rs, rx, n0,
+                       K, u.k_beg + (c + kRingStages - 1) * kRingKC, u.k_end, wave, lane);
+      ring_compute<BM>(acc, ring + (c % kRingStages) * L::kStage, wave, lane);
+    }
+    __syncthreads();  // every wave is done with the ring before the next unit refills it
+    finish_tile<NF, kRingNW, kRingWaves>(acc, p, u, sc);
+  }
+}
+
+// ---- register kernel (any k % 16 == 0) ------------------------------------------
+
+constexpr int kRegThreads = 256;   // 4 waves
+constexpr int kRegWaves = kRegThreads / kWave;
+constexpr int kNW = 4;             // MFMA column tiles per wave
+constexpr int kKC = 256;           // K per chunk
+constexpr int kLdsStride = kKC + 8;  // BF16 elements per staged activation row (16 B pad)
+
+// One lane's packed weights (8 dwords = 64 nibbles along K) and its 4 block
+// scales for each of the wave's kNW column tiles, for one 256-wide K chunk.
+struct WTile {
+  uint32_t w[kNW][8];
+  uint32_t s[kNW];
+};
+
+__device__ __forceinline__ void load_wtile(WTile& t, __amdgpu_buffer_rsrc_t rw,
+                                           __amdgpu_buffer_rsrc_t rs, const int (&nrow)[kNW],
+                                           int K, int kpos, int k_end) {
+#pragma unroll
+  for (int j = 0; j < kNW; ++j) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int kd = kpos + 8 * u;
+      const uint32_t o = kd < k_end ? (uint32_t)nrow[j] * (uint32_t)(K / 2) + (uint32_t)(kd / 2)
+                                    : kOffNone;
+      t.w[j][u] = __builtin_amdgcn_raw_buffer_load_b32(rw, o, 0, 0);
+    }
+    uint32_t sv = 0u;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int kb = kpos + 16 * b;
+      const uint32_t o = kb < k_end ? (uint32_t)nrow[j] * (uint32_t)(K / 16) + (uint32_t)(kb / 16)
+                                    : kOffNone;
+      sv |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs, o, 0, 0) << (8 * b);
+    }
+    t.s[j] = sv;
+  }
+}
+
+// Activation chunk [row0, row0 + BM) x [kc, kc + 256): 16-byte pieces, one
+// per thread per pass, zero outside the segment / split.
+template <int BM>
+__device__ __forceinline__ void load_xtile(u32x4_t (&xr)[BM / 8], const uint16_t* __restrict__ x,
+                                           int row0, int row_end, int K, int kc, int k_end,
+                                           int tid) {
+#pragma unroll
+  for (int pass = 0; pass < BM / 8; ++pass) {
+    const int pc = tid + kRegThreads * pass;
+    const int grow = row0 + (pc >> 5);
+    const int kk = kc + (pc & 31) * 8;
+    xr[pass] = u32x4_t{0u, 0u, 0u, 0u};
+    if (grow < row_end && kk < k_end)
+      xr[pass] = *reinterpret_cast<const u32x4_t*>(x + (int64_t)grow * K + kk);
+  }
+}
+
+template <int BM>
+__device__ __forceinline__ void store_xtile(uint16_t* xs, const u32x4_t (&xr)[BM / 8], int tid) {
+#pragma unroll
+  for (int pass = 0; pass < BM / 8; ++pass) {
+    const int pc = tid + kRegThreads * pass;
+    *reinterpret_cast<u32x4_t*>(&xs[(pc >> 5) * kLdsStride + (pc & 31) * 8]) = xr[pass];
+  }
+}
+
+// 8 MFMA steps of 32 K slots over one staged chunk; lane group q supplies
+// K = kc + 64q + 8i .. +7 in step i.
+template <int BM>
+__device__ __forceinline__ void reg_compute(f32x4_t (&acc)[BM / 16][kNW], const uint16_t* xs,
+                                            const WTile& t, int q, int r16) {
+  constexpr int NF = BM / 16;
+  float scl[kNW][4];
+#pragma unroll
+  for (int j = 0; j < kNW; ++j) {
+    scl[j][0] = decode_e4m3<0>(t.s[j]);
+    scl[j][1] = decode_e4m3<1>(t.s[j]);
+    scl[j][2] = decode_e4m3<2>(t.s[j]);
+    scl[j][3] = decode_e4m3<3>(t.s[j]);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    bf16x8_t a[NF];
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+      a[f] = *reinterpret_cast<const bf16x8_t*>(&xs[(f * 16 + r16) * kLdsStride + 64 * q + 8 * i]);
+#pragma unroll
+    for (int j = 0; j < kNW; ++j) {
+      const bf16x8_t b = dequant8(t.w[j][i], scl[j][i >> 1]);
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+        acc[f][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[f], b, acc[f][j], 0, 0, 0);
+    }
+  }
+}
+
+template <int BM>
+__global__ __launch_bounds__(kRegThreads) void gemm_reg_kernel(GemmParams p) {
+  constexpr int NF = BM / 16;
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM * kLdsStride];
+  __shared__ Sched sc;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q = lane >> 4, r16 = lane & 15;
+  const int total = build_schedule<kRegThreads, BM>(sc, p);
+  const int N = p.n, K = p.k;
+
+  for (int unit = blockIdx.x; unit < total; unit += gridDim.x) {
+    const Unit u = decode_unit<BM>(sc, p, unit);
+    const __amdgpu_buffer_rsrc_t rw =
+        make_rsrc(p.w + (int64_t)u.e * N * (K / 2), (uint32_t)N * (uint32_t)(K / 2));
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(p.s + (int64_t)u.e * N * (K / 16), (uint32_t)N * (uint32_t)(K / 16));
     int nrow[kNW];
 #pragma unroll
-    for (int j = 0; j < kNW; ++j) nrow[j] = nt * kBN + wave * (kNW * 16) + j * 16 + r16;
+    for (int j = 0; j < kNW; ++j) nrow[j] = u.nt * kBN + wave * (kNW * 16) + j * 16 + r16;
 
     f32x4_t acc[NF][kNW];
 #pragma unroll
@@ -165,153 +553,40 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmParams p) {
 #pragma unroll
       for (int j = 0; j < kNW; ++j) acc[f][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    for (int kc = k_beg; kc < k_end; kc += kKC) {
-      // -- this lane's packed weights and scales for the chunk
-      uint32_t wreg[kNW][8];
-      uint32_t sreg[kNW];
-      const int kpos = kc + 64 * q;
-#pragma unroll
-      for (int j = 0; j < kNW; ++j) {
-        const bool rv = nrow[j] < N;
-        if (FAST) {
-          if (rv && kpos < k_end) {
-            const u32x4_t* src =
-                reinterpret_cast<const u32x4_t*>(We + (int64_t)nrow[j] * (K / 2) + kpos / 2);
-            const u32x4_t a = __builtin_nontemporal_load(src);
-            const u32x4_t b = __builtin_nontemporal_load(src + 1);
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              wreg[j][t] = a[t];
-              wreg[j][4 + t] = b[t];
-            }
-            sreg[j] = *reinterpret_cast<const uint32_t*>(Se + (int64_t)nrow[j] * (K / 16) +
-                                                         kpos / 16);
-          } else {
-#pragma unroll
-            for (int t = 0; t < 8; ++t) wreg[j][t] = 0u;
-            sreg[j] = 0u;
-          }
-        } else {
-          uint32_t sv = 0u;
-#pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            const int kd = kpos + 8 * t;
-            wreg[j][t] = (rv && kd < k_end)
-                             ? *reinterpret_cast<const uint32_t*>(
-                                   We + (int64_t)nrow[j] * (K / 2) + kd / 2)
-                             : 0u;
-          }
-#pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const int kb = kpos + 16 * b;
-            const uint32_t byte =
-                (rv && kb < k_end) ? (uint32_t)Se[(int64_t)nrow[j] * (K / 16) + kb / 16] : 0u;
-            sv |= byte << (8 * b);
-          }
-          sreg[j] = sv;
-        }
+    // two-stage pipeline: chunk c+1's weights (registers) and activations
+    // (registers, then LDS) are in flight while chunk c is multiplied out
+    const int nch = (u.k_end - u.k_beg + kKC - 1) / kKC;
+    WTile wa, wb;
+    u32x4_t xr[BM / 8];
+    load_wtile(wa, rw, rs, nrow, K, u.k_beg + 64 * q, u.k_end);
+    load_xtile<BM>(xr, p.x, u.row0, u.row_end, K, u.k_beg, u.k_end, tid);
+    store_xtile<BM>(xs[0], xr, tid);
+    __syncthreads();
+    for (int c = 0; c < nch; c += 2) {
+      const int kc = u.k_beg + c * kKC;
+      const bool more1 = c + 1 < nch;
+      if (more1) {
+        load_wtile(wb, rw, rs, nrow, K, kc + kKC + 64 * q, u.k_end);
+        load_xtile<BM>(xr, p.x, u.row0, u.row_end, K, kc + kKC, u.k_end, tid);
       }
-
-      // -- stage the activation chunk [row0, row0+BM) x [kc, kc+256) in LDS
-#pragma unroll
-      for (int pass = 0; pass < BM / 8; ++pass) {
-        const int pc = tid + kGemmThreads * pass;
-        const int r = pc >> 5;
-        const int c8 = (pc & 31) * 8;
-        const int grow = row0 + r;
-        const int kk = kc + c8;
-        u32x4_t v = {0u, 0u, 0u, 0u};
-        if (grow < row_end && kk < k_end)
-          v = *reinterpret_cast<const u32x4_t*>(p.x + (int64_t)grow * K + kk);
-        *reinterpret_cast<u32x4_t*>(&xs[r * kLdsStride + c8]) = v;
-      }
+      reg_compute<BM>(acc, xs[0], wa, q, r16);
+      if (more1) store_xtile<BM>(xs[1], xr, tid);
       __syncthreads();
-
-      // -- 8 MFMA steps of 32 K slots
-      float sc[kNW][4];
-#pragma unroll
-      for (int j = 0; j < kNW; ++j) {
-        sc[j][0] = decode_e4m3<0>(sreg[j]);
-        sc[j][1] = decode_e4m3<1>(sreg[j]);
-        sc[j][2] = decode_e4m3<2>(sreg[j]);
-        sc[j][3] = decode_e4m3<3>(sreg[j]);
+      if (!more1) break;
+      const bool more2 = c + 2 < nch;
+      if (more2) {
+        load_wtile(wa, rw, rs, nrow, K, kc + 2 * kKC + 64 * q, u.k_end);
+        load_xtile<BM>(xr, p.x, u.row0, u.row_end, K, kc + 2 * kKC, u.k_end, tid);
       }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        bf16x8_t a[NF];
-#pragma unroll
-        for (int f = 0; f < NF; ++f)
-          a[f] = *reinterpret_cast<const bf16x8_t*>(
-              &xs[(f * 16 + r16) * kLdsStride + 64 * q + 8 * i]);
-#pragma unroll
-        for (int j = 0; j < kNW; ++j) {
-          const bf16x8_t b = dequant8(wreg[j][i], sc[j][i >> 1]);
-#pragma unroll
-          for (int f = 0; f < NF; ++f)
-            acc[f][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[f], b, acc[f][j], 0, 0, 0);
-        }
-      }
+      reg_compute<BM>(acc, xs[1], wb, q, r16);
+      if (more2) store_xtile<BM>(xs[0], xr, tid);
       __syncthreads();
     }
-
-    // ---- split-K hand-off --------------------------------------------------
-    if (S > 1) {
-      float* part = p.partials + (int64_t)tile * S * (BM * kBN);
-#pragma unroll
-      for (int f = 0; f < NF; ++f)
-#pragma unroll
-        for (int j = 0; j < kNW; ++j)
-          *reinterpret_cast<f32x4_t*>(part + (int64_t)ks * (BM * kBN) +
-                                      (((wave * NF + f) * kNW + j) * kWave + lane) * 4) =
-              acc[f][j];
-      fence_release_agent();
-      __syncthreads();
-      if (tid == 0) {
-        const uint32_t old = atomicAdd(&p.counters[tile], 1u);
-        s_flag = (old == (uint32_t)(S - 1));
-      }
-      __syncthreads();
-      if (!s_flag) continue;
-      fence_acquire_agent();
-#pragma unroll
-      for (int f = 0; f < NF; ++f)
-#pragma unroll
-        for (int j = 0; j < kNW; ++j) {
-          f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
-          for (int s = 0; s < S; ++s) {
-            f32x4_t v = (s == ks) ? acc[f][j]
-                                  : __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(
-                                        part + (int64_t)s * (BM * kBN) +
-                                        (((wave * NF + f) * kNW + j) * kWave + lane) * 4));
-            sum = (s == 0) ? v : sum + v;
-          }
-          acc[f][j] = sum;
-        }
-      if (tid == 0) p.counters[tile] = 0u;
-    }
-
-    // ---- epilogue: y = g * acc ----------------------------------------------
-    const float gv = p.g[e];
-#pragma unroll
-    for (int f = 0; f < NF; ++f)
-#pragma unroll
-      for (int j = 0; j < kNW; ++j) {
-        const int col = nrow[j];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = row0 + f * 16 + 4 * q + r;
-          if (row < row_end && col < N) {
-            const float v = gv * acc[f][j][r];
-            if (p.out_f32)
-              reinterpret_cast<float*>(p.y)[(int64_t)row * N + col] = v;
-            else
-              reinterpret_cast<uint16_t*>(p.y)[(int64_t)row * N + col] =
-                  (uint16_t)float_to_bf16_rne(v);
-          }
-        }
-      }
+    finish_tile<NF, kNW, kRegWaves>(acc, p, u, sc);
   }
 }
+
+// ---- host side -----------------------------------------------------------------
 
 __global__ void fill_zero_kernel(u32x4_t* __restrict__ p, size_t n16) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
@@ -329,26 +604,30 @@ hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int BM, bool FAST>
-static int occupancy() {
-  static int occ = -1;
-  if (occ < 0) {
-    int v = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, gemm_kernel<BM, FAST>, kGemmThreads,
-                                                     0) != hipSuccess ||
-        v < 1)
-      v = 1;
-    occ = v;
-  }
-  return occ;
+template <typename KernelT>
+static int occupancy_of(KernelT kernel, int threads) {
+  int v = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, kernel, threads, 0) != hipSuccess || v < 1)
+    v = 1;
+  return v;
 }
 
-static int occupancy_for(int bm, bool fast) {
-  switch (bm) {
-    case 16: return fast ? occupancy<16, true>() : occupancy<16, false>();
-    case 32: return fast ? occupancy<32, true>() : occupancy<32, false>();
-    default: return fast ? occupancy<64, true>() : occupancy<64, false>();
+static int occupancy_for(int bm, bool ring) {
+  static int cache[2][3] = {{-1, -1, -1}, {-1, -1, -1}};
+  const int bi = bm == 16 ? 0 : (bm == 32 ? 1 : 2);
+  int& c = cache[ring ? 1 : 0][bi];
+  if (c < 0) {
+    if (ring) {
+      c = bm == 16 ? occupancy_of(gemm_ring_kernel<16>, kRingThreads)
+                   : bm == 32 ? occupancy_of(gemm_ring_kernel<32>, kRingThreads)
+                              : occupancy_of(gemm_ring_kernel<64>, kRingThreads);
+    } else {
+      c = bm == 16 ? occupancy_of(gemm_reg_kernel<16>, kRegThreads)
+                   : bm == 32 ? occupancy_of(gemm_reg_kernel<32>, kRegThreads)
+                              : occupancy_of(gemm_reg_kernel<64>, kRegThreads);
+    }
   }
+  return c;
 }
 
 static int env_int(const char* name, int dflt) {
@@ -378,12 +657,13 @@ GemmPlan plan_gemm(int64_t rows, int64_t num_experts, int64_t n, int64_t k, bool
   const int64_t slots = (int64_t)cu_count * occ;
   // Split K only when there are too few tiles to occupy the resident slots.
   const int align = pl.fast ? 64 : 16;
+  const int kc = pl.fast ? kRingKC : kKC;
   int splits = 1;
   const int64_t tiles_est = grouped ? std::min<int64_t>(num_experts, rows) * pl.n_tiles
                                     : max_tiles;
   if (tiles_est < slots) {
     int64_t want = (slots + tiles_est - 1) / tiles_est;
-    const int64_t kmax = std::max<int64_t>(1, k / kKC);
+    const int64_t kmax = std::max<int64_t>(1, k / (2 * kc));
     splits = (int)std::min<int64_t>(want, kmax);
   }
   const int force_s = env_int("NVFP4_SPLITK", 0);
@@ -403,19 +683,18 @@ GemmPlan plan_gemm(int64_t rows, int64_t num_experts, int64_t n, int64_t k, bool
 }
 
 hipError_t launch_gemm(const GemmPlan& pl, const GemmParams& p, hipStream_t stream) {
-  dim3 grid(pl.grid), block(kGemmThreads);
-#define NVFP4_LAUNCH(BMV, FV) \
-  hipLaunchKernelGGL((gemm_kernel<BMV, FV>), grid, block, 0, stream, p)
+  dim3 grid(pl.grid);
   if (pl.fast) {
-    if (pl.bm == 16) NVFP4_LAUNCH(16, true);
-    else if (pl.bm == 32) NVFP4_LAUNCH(32, true);
-    else NVFP4_LAUNCH(64, true);
+    dim3 block(kRingThreads);
+    if (pl.bm == 16) hipLaunchKernelGGL(gemm_ring_kernel<16>, grid, block, 0, stream, p);
+    else if (pl.bm == 32) hipLaunchKernelGGL(gemm_ring_kernel<32>, grid, block, 0, stream, p);
+    else hipLaunchKernelGGL(gemm_ring_kernel<64>, grid, block, 0, stream, p);
   } else {
-    if (pl.bm == 16) NVFP4_LAUNCH(16, false);
-    else if (pl.bm == 32) NVFP4_LAUNCH(32, false);
-    else NVFP4_LAUNCH(64, false);
+    dim3 block(kRegThreads);
+    if (pl.bm == 16) hipLaunchKernelGGL(gemm_reg_kernel<16>, grid, block, 0, stream, p);
+    else if (pl.bm == 32) hipLaunchKernelGGL(gemm_reg_kernel<32>, grid, block, 0, stream, p);
+    else hipLaunchKernelGGL(gemm_reg_kernel<64>, grid, block, 0, stream, p);
   }
-#undef NVFP4_LAUNCH
   return hipGetLastError();
 }
 

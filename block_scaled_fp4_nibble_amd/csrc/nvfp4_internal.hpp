@@ -20,11 +20,8 @@ hipError_t launch_quantize(const uint16_t* w, int64_t batch, int64_t n, int64_t 
                            uint32_t* partial, int parts, hipStream_t stream);
 
 // ---- GEMM ---------------------------------------------------------------
-// Column tile of one workgroup (4 waves x 4 MFMA column tiles x 16).
-constexpr int kGemmThreads = 256;
+// Output columns (weight rows) covered by one work unit.
 constexpr int kBN = 256;
-// K covered by one staged activation chunk.
-constexpr int kKC = 256;
 
 struct GemmParams {
   const uint16_t* x;        // [rows][k] bf16

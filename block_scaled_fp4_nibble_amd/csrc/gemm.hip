@@ -80,27 +80,17 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)(p);
 }
 
-__device__ __forceinline__ void lds_dma16(uint32_t lds, uint32_t voff, u32x4_t rsrc) {
+__device__ __forceinline__ void lds_dma16(uint32_t lds, uint32_t voff, uint32_t soff,
+                                          u32x4_t rsrc) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %1\n\t"
-      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc)
-      : "memory");
-}
-
-__device__ __forceinline__ void lds_dma4(uint32_t lds, uint32_t voff, u32x4_t rsrc) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "buffer_load_dword %2, %3, 0 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc)
+      : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc),
+        "s"(__builtin_amdgcn_readfirstlane(soff))
       : "memory");
 }
 
@@ -277,123 +267,190 @@ __device__ __forceinline__ bool finish_tile(f32x4_t (&acc)[NF][NW], const GemmPa
 
 // ---- ring kernel (k % 64 == 0) ------------------------------------------------
 
-constexpr int kRingThreads = 512;  // 8 waves
-constexpr int kRingWaves = kRingThreads / kWave;
-constexpr int kRingNW = 2;         // MFMA column tiles per wave
+// A ring workgroup has WAVES = 8 or 16 waves; each owns 256 / WAVES of the
+// unit's columns, i.e. NW = 16 / WAVES MFMA column tiles.
 constexpr int kRingKC = 128;       // K per stage
 constexpr int kRingStages = 4;
 
-template <int BM>
+template <int BM, int WAVES>
 struct RingLayout {
+  static constexpr int kNW = 16 / WAVES;            // MFMA column tiles per wave
+  static constexpr int kWPerWave = 16 / WAVES;      // 1 KB weight loads per wave per stage
   static constexpr int kW = 0;                      // 256 rows x 64 B packed nibbles
-  static constexpr int kS = kW + kBN * 64;          // 256 rows x 8 scale bytes
-  static constexpr int kX = kS + kBN * 8;           // BM rows x 256 B activations
+  static constexpr int kX = kW + kBN * 64;          // BM rows x 256 B activations
   static constexpr int kStage = kX + BM * 256;
   static constexpr int kXInstr = BM / 4;            // 1 KB (4-row) loads per stage
-  static constexpr int kXPerWave = kXInstr >= kRingWaves ? kXInstr / kRingWaves : 1;
-  static constexpr int kLoadsPerWave = 2 + 1 + kXPerWave;
+  static constexpr int kXPerWave = kXInstr >= WAVES ? kXInstr / WAVES : 1;
+  static constexpr int kLoadsPerStage = kWPerWave + kXPerWave;  // per wave
+  // Block scales arrive in windows of 4 stages (512 K = 32 bytes per row), two
+  // window slots: one 1 KB load per wave per window instead of 8-byte row
+  // pieces every stage.
+  static constexpr int kWinStages = 4;
+  static constexpr int kWinBytes = kBN * 32;
+  static constexpr int kSWin = kRingStages * kStage;
+  static constexpr int kTotal = kSWin + 2 * kWinBytes;
 };
 
-__device__ __forceinline__ void wait_vmcnt_stages(int stages_after, int per_stage) {
-  // s_waitcnt vmcnt(stages_after * per_stage): the immediate must be a
-  // constant, so the possible counts are spelled out.  Encoding (gfx9):
-  // vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt and lgkmcnt
-  // left at their maxima (no wait on them).
-#define NVFP4_VMCNT(n) \
-  __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
-  const int n = stages_after * per_stage;
-  if (n == 4) NVFP4_VMCNT(4);
-  else if (n == 5) NVFP4_VMCNT(5);
-  else if (n == 8) NVFP4_VMCNT(8);
-  else if (n == 10) NVFP4_VMCNT(10);
-  else NVFP4_VMCNT(0);
+// s_waitcnt vmcnt(n) for a run-time n in [0, 15]: the immediate must be a
+// constant.  Encoding (gfx9): vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits
+// 15:14, expcnt and lgkmcnt left at their maxima (no wait on them).
+__device__ __forceinline__ void wait_vmcnt(int n) {
+#define NVFP4_VMCNT(v) \
+  case v: __builtin_amdgcn_s_waitcnt(((v) & 15) | (((v) >> 4) << 14) | (7 << 4) | (15 << 8)); break;
+  switch (n) {
+    NVFP4_VMCNT(1) NVFP4_VMCNT(2) NVFP4_VMCNT(3) NVFP4_VMCNT(4) NVFP4_VMCNT(5) NVFP4_VMCNT(6)
+    NVFP4_VMCNT(7) NVFP4_VMCNT(8) NVFP4_VMCNT(9) NVFP4_VMCNT(10) NVFP4_VMCNT(11)
+    NVFP4_VMCNT(12) NVFP4_VMCNT(13) NVFP4_VMCNT(14) NVFP4_VMCNT(15)
+    default: __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8)); break;
+  }
 #undef NVFP4_VMCNT
 }
 
-// Issue the loads of one stage (K range [kc, kc + 128) of the unit) into LDS.
-template <int BM>
-__device__ __forceinline__ void ring_issue(uint32_t stage, u32x4_t rw, u32x4_t rs, u32x4_t rx,
-                                           int n0, int K, int kc, int k_end, int wave, int lane) {
-  using L = RingLayout<BM>;
-  // packed weights: 16 loads of 1 KB = 16 rows x 64 B; lane -> (row, slot),
-  // slot s of row R holds the row's 16-byte piece s ^ ((R >> 1) & 3)
+// Per-lane constant parts of a unit's load offsets (the K position of a
+// stage goes into the instruction's scalar offset).
+template <int BM, int WAVES>
+struct RingOffsets {
+  uint32_t w[16 / WAVES];                           // weight pieces
+  uint32_t x[RingLayout<BM, WAVES>::kXPerWave];     // activation pieces
+  int xk[RingLayout<BM, WAVES>::kXPerWave];         // K of the piece within a stage
+  uint32_t s;                                       // scale window piece
+};
+
+template <int BM, int WAVES>
+__device__ __forceinline__ RingOffsets<BM, WAVES> ring_offsets(int n0, int K, int wave,
+                                                               int lane) {
+  using L = RingLayout<BM, WAVES>;
+  RingOffsets<BM, WAVES> o;
+  // weights: load t covers rows 16t..16t+15, 64 B each; slot s of row R holds
+  // the row's 16-byte piece s ^ ((R >> 1) & 3)
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    const int t = wave * 2 + tt;
+  for (int tt = 0; tt < L::kWPerWave; ++tt) {
+    const int t = wave * L::kWPerWave + tt;
     const int R = t * 16 + (lane >> 2);
     const int g = (lane & 3) ^ ((R >> 1) & 3);
-    const int kp = kc + 32 * g;
-    const uint32_t off = kp < k_end ? (uint32_t)(n0 + R) * (uint32_t)(K / 2) + (uint32_t)(kp / 2)
-                                    : kOffNone;
-    lds_dma16(stage + L::kW + t * 1024, off, rw);
+    o.w[tt] = (uint32_t)(n0 + R) * (uint32_t)(K / 2) + (uint32_t)(16 * g);
   }
-  // block scales: 8 loads of 256 B = 32 rows x 8 B, 4 bytes (4 blocks) per lane
-  {
-    const int R = wave * 32 + (lane >> 1);
-    const int kb = kc + 64 * (lane & 1);
-    const uint32_t off = kb < k_end ? (uint32_t)(n0 + R) * (uint32_t)(K / 16) + (uint32_t)(kb / 16)
-                                    : kOffNone;
-    lds_dma4(stage + L::kS + wave * 256, off, rs);
-  }
-  // activations: BM/4 loads of 1 KB = 4 rows x 256 B; slot s of row r holds
-  // piece s ^ (r & 7).  With fewer loads than waves, waves repeat a load
-  // (same bytes to the same place) so every wave issues the same count.
+  // activations: load t covers rows 4t..4t+3, 256 B each; slot s of row r
+  // holds piece s ^ (r & 7).  With fewer loads than waves, waves repeat a
+  // load (same bytes to the same place) so every wave issues the same count.
 #pragma unroll
   for (int tt = 0; tt < L::kXPerWave; ++tt) {
-    const int t = L::kXInstr >= kRingWaves ? wave * L::kXPerWave + tt : wave % L::kXInstr;
+    const int t = L::kXInstr >= WAVES ? wave * L::kXPerWave + tt : wave % L::kXInstr;
     const int r = t * 4 + (lane >> 4);
     const int g = (lane & 15) ^ (r & 7);
-    const int kk = kc + 8 * g;
-    const uint32_t off = kk < k_end ? (uint32_t)r * (uint32_t)(K * 2) + (uint32_t)(kk * 2)
-                                    : kOffNone;
-    lds_dma16(stage + L::kX + t * 1024, off, rx);
+    o.x[tt] = (uint32_t)r * (uint32_t)(K * 2) + (uint32_t)(16 * g);
+    o.xk[tt] = 8 * g;
+  }
+  // scale window: eight 1 KB loads of 32 rows x 32 bytes; with 16 waves,
+  // waves 8-15 repeat the loads of waves 0-7
+  {
+    const int R = (wave & 7) * 32 + (lane >> 1);
+    o.s = (uint32_t)(n0 + R) * (uint32_t)(K / 16) + (uint32_t)(16 * (lane & 1));
+  }
+  return o;
+}
+
+// Issue one stage (K range [kc, kc + 128) of the unit) into LDS.  Weight
+// pieces past the split end are loaded anyway (their block scales are taken
+// as 0 when multiplied); activation pieces past it read as zero.
+template <int BM, int WAVES>
+__device__ __forceinline__ void ring_issue(uint32_t stage, u32x4_t rw, u32x4_t rx,
+                                           const RingOffsets<BM, WAVES>& o, int K, int kc,
+                                           int k_end, int wave) {
+  using L = RingLayout<BM, WAVES>;
+#pragma unroll
+  for (int tt = 0; tt < L::kWPerWave; ++tt)
+    lds_dma16(stage + L::kW + (wave * L::kWPerWave + tt) * 1024, o.w[tt], (uint32_t)(kc / 2), rw);
+  const bool tail = kc + kRingKC > k_end;
+#pragma unroll
+  for (int tt = 0; tt < L::kXPerWave; ++tt) {
+    const int t = L::kXInstr >= WAVES ? wave * L::kXPerWave + tt : wave % L::kXInstr;
+    const uint32_t voff = (tail && kc + o.xk[tt] >= k_end) ? kOffNone : o.x[tt];
+    lds_dma16(stage + L::kX + t * 1024, voff, (uint32_t)(kc * 2), rx);
   }
 }
 
-// Multiply out one staged 128-wide K range: 4 MFMA steps of 32 K slots.
-// Lane group q supplies K = kc + 32q + 8i .. +7 in step i.
-template <int BM>
-__device__ __forceinline__ void ring_compute(f32x4_t (&acc)[BM / 16][kRingNW],
-                                             const uint8_t* stage, int wave, int lane) {
-  using L = RingLayout<BM>;
+// Issue the scale window [kw, kw + 512) of the unit (one 1 KB load per wave).
+__device__ __forceinline__ void ring_issue_scales(uint32_t slot, u32x4_t rs, uint32_t soff_lane,
+                                                  int kw, int wave) {
+  lds_dma16(slot + (wave & 7) * 1024, soff_lane, (uint32_t)(kw / 16), rs);
+}
+
+// One stage's operands, read from LDS into registers one iteration ahead.
+template <int BM, int WAVES>
+struct StageRegs {
+  u32x4_t wd[16 / WAVES];
+  uint32_t s2[16 / WAVES];
+  bf16x8_t a[4][BM / 16];
+};
+
+// Lane group q supplies K = kc + 32q + 8i .. +7 in MFMA step i; its two block
+// scales sit at byte 8 * (stage index within the window) + 2q of the row's
+// window entry.  Scales of K slots past the split end are taken as 0 (their
+// weight nibbles may belong to the next split).
+template <int BM, int WAVES>
+__device__ __forceinline__ void ring_read(StageRegs<BM, WAVES>& r, const uint8_t* stage,
+                                          const uint8_t* swin, int sub, bool kvalid, int wave,
+                                          int lane) {
+  using L = RingLayout<BM, WAVES>;
   constexpr int NF = BM / 16;
   const int q = lane >> 4, r16 = lane & 15;
-  u32x4_t wd[kRingNW];
-  float scl[kRingNW][2];
 #pragma unroll
-  for (int j = 0; j < kRingNW; ++j) {
-    const int R = wave * (kRingNW * 16) + j * 16 + r16;
-    wd[j] = *reinterpret_cast<const u32x4_t*>(stage + L::kW + R * 64 + 16 * (q ^ ((R >> 1) & 3)));
-    const uint32_t s2 = *reinterpret_cast<const uint16_t*>(stage + L::kS + R * 8 + 2 * q);
-    scl[j][0] = decode_e4m3<0>(s2);
-    scl[j][1] = decode_e4m3<1>(s2);
+  for (int j = 0; j < L::kNW; ++j) {
+    const int R = wave * (L::kNW * 16) + j * 16 + r16;
+    r.wd[j] = *reinterpret_cast<const u32x4_t*>(stage + L::kW + R * 64 + 16 * (q ^ ((R >> 1) & 3)));
+    const uint32_t s2 = *reinterpret_cast<const uint16_t*>(swin + R * 32 + 8 * sub + 2 * q);
+    r.s2[j] = kvalid ? s2 : 0u;
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    bf16x8_t a[NF];
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int f = 0; f < NF; ++f)
-      a[f] = *reinterpret_cast<const bf16x8_t*>(stage + L::kX + (f * 16 + r16) * 256 +
-                                                16 * ((4 * q + i) ^ (r16 & 7)));
-#pragma unroll
-    for (int j = 0; j < kRingNW; ++j) {
-      const bf16x8_t b = dequant8(wd[j][i], scl[j][i >> 1]);
-#pragma unroll
-      for (int f = 0; f < NF; ++f)
-        acc[f][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[f], b, acc[f][j], 0, 0, 0);
-    }
-  }
+      r.a[i][f] = *reinterpret_cast<const bf16x8_t*>(stage + L::kX + (f * 16 + r16) * 256 +
+                                                     16 * ((4 * q + i) ^ (r16 & 7)));
 }
 
-template <int BM>
-__global__ __launch_bounds__(kRingThreads) void gemm_ring_kernel(GemmParams p) {
-  using L = RingLayout<BM>;
+// Multiply out one stage held in registers: 4 MFMA steps of 32 K slots.
+template <int BM, int WAVES>
+__device__ __forceinline__ void ring_mma(f32x4_t (&acc)[BM / 16][16 / WAVES],
+                                         const StageRegs<BM, WAVES>& r) {
+  constexpr int NF = BM / 16, NW = 16 / WAVES;
+  float scl[NW][2];
+#pragma unroll
+  for (int j = 0; j < NW; ++j) {
+    scl[j][0] = decode_e4m3<0>(r.s2[j]);
+    scl[j][1] = decode_e4m3<1>(r.s2[j]);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < NW; ++j) {
+      const bf16x8_t b = dequant8(r.wd[j][i], scl[j][i >> 1]);
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+        acc[f][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.a[i][f], b, acc[f][j], 0, 0, 0);
+    }
+}
+
+// Pipeline per unit (per wave, in issue order): scale window 0, stages
+// 0..2; then iteration c waits for stage c, passes the barrier, issues stage
+// c+3 into the slot of stage c-1 plus, when c % 4 == 0, scale window c/4 + 1,
+// and multiplies out stage c (three stages in flight meanwhile).
+template <int BM, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void gemm_ring_kernel(GemmParams p) {
+  using L = RingLayout<BM, WAVES>;
   constexpr int NF = BM / 16;
-  __shared__ __attribute__((aligned(16))) uint8_t ring[kRingStages * L::kStage];
+  constexpr int NW = L::kNW;
+  constexpr int WS = L::kWinStages;
+  constexpr int LS = L::kLoadsPerStage;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[L::kTotal];
   __shared__ Sched sc;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int total = build_schedule<kRingThreads, BM>(sc, p);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int total = build_schedule<WAVES * 64, BM>(sc, p);
   const int N = p.n, K = p.k;
+  const uint32_t ring0 = lds_addr(ring);
+  const int q = lane >> 4;
 
   for (int unit = blockIdx.x; unit < total; unit += gridDim.x) {
     const Unit u = decode_unit<BM>(sc, p, unit);
@@ -404,31 +461,46 @@ __global__ __launch_bounds__(kRingThreads) void gemm_ring_kernel(GemmParams p) {
         rsrc_words(p.s + (int64_t)u.e * N * (K / 16), (uint32_t)N * (uint32_t)(K / 16));
     const u32x4_t rx =
         rsrc_words(p.x + (int64_t)u.row0 * K, (uint32_t)(u.row_end - u.row0) * (uint32_t)(K * 2));
-    const uint32_t ring0 = lds_addr(ring);
+    const RingOffsets<BM, WAVES> off = ring_offsets<BM, WAVES>(n0, K, wave, lane);
 
-    f32x4_t acc[NF][kRingNW];
+    f32x4_t acc[NF][NW];
 #pragma unroll
     for (int f = 0; f < NF; ++f)
 #pragma unroll
-      for (int j = 0; j < kRingNW; ++j) acc[f][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < NW; ++j) acc[f][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     const int nch = (u.k_end - u.k_beg + kRingKC - 1) / kRingKC;
+    const int nwin = (nch + WS - 1) / WS;
+    ring_issue_scales(ring0 + L::kSWin, rs, off.s, u.k_beg, wave);
     for (int s = 0; s < kRingStages - 1 && s < nch; ++s)
-      ring_issue<BM>(ring0 + s * L::kStage, rw, rs, rx, n0, K, u.k_beg + s * kRingKC, u.k_end,
-                     wave, lane);
+      ring_issue<BM, WAVES>(ring0 + s * L::kStage, rw, rx, off, K, u.k_beg + s * kRingKC,
+                            u.k_end, wave);
     for (int c = 0; c < nch; ++c) {
-      // this wave's loads for stage c have landed once at most the loads of
-      // the (up to two) later stages are outstanding; the barrier extends
-      // that to every wave's loads and retires everyone's reads of stage c-1
-      wait_vmcnt_stages(min(kRingStages - 2, nch - 1 - c), L::kLoadsPerWave);
+      // Loads this wave issued after stage c: the (up to two) later stages,
+      // plus any window issued at iterations c-3 .. c-1.  Waiting until only
+      // those are outstanding means stage c (and the window it reads, issued
+      // earlier) has landed; the barrier extends that to every wave's loads
+      // and retires everyone's reads of stage c-1.
+      int after = LS * (min(nch - 1, c + 2) - c);
+      for (int i = max(0, c - 3); i < c; ++i) after += (i % WS == 0 && i / WS + 1 < nwin) ? 1 : 0;
+      wait_vmcnt(after);
       __syncthreads();
       if (c + kRingStages - 1 < nch)
-        ring_issue<BM>(ring0 + ((c + kRingStages - 1) % kRingStages) * L::kStage, rw, rs, rx, n0,
-                       K, u.k_beg + (c + kRingStages - 1) * kRingKC, u.k_end, wave, lane);
-      ring_compute<BM>(acc, ring + (c % kRingStages) * L::kStage, wave, lane);
+        ring_issue<BM, WAVES>(ring0 + ((c + kRingStages - 1) % kRingStages) * L::kStage, rw, rx,
+                              off, K, u.k_beg + (c + kRingStages - 1) * kRingKC, u.k_end, wave);
+      // window c/4 + 1 reuses the slot of window c/4 - 1, which every wave
+      // finished before this barrier; it is first read four iterations later
+      if (c % WS == 0 && c / WS + 1 < nwin)
+        ring_issue_scales(ring0 + L::kSWin + ((c / WS + 1) & 1) * L::kWinBytes, rs, off.s,
+                          u.k_beg + (c / WS + 1) * WS * kRingKC, wave);
+      StageRegs<BM, WAVES> r;
+      ring_read<BM, WAVES>(r, ring + (c % kRingStages) * L::kStage,
+                           ring + L::kSWin + ((c / WS) & 1) * L::kWinBytes, c % WS,
+                           u.k_beg + c * kRingKC + 32 * q < u.k_end, wave, lane);
+      ring_mma<BM, WAVES>(acc, r);
     }
     __syncthreads();  // every wave is done with the ring before the next unit refills it
-    finish_tile<NF, kRingNW, kRingWaves>(acc, p, u, sc);
+    finish_tile<NF, NW, WAVES>(acc, p, u, sc);
   }
 }
 
@@ -612,15 +684,31 @@ static int occupancy_of(KernelT kernel, int threads) {
   return v;
 }
 
+static int env_int(const char* name, int dflt) {
+  const char* v = getenv(name);
+  if (!v || !*v) return dflt;
+  return atoi(v);
+}
+
+static int ring_waves() {
+  const int w = env_int("NVFP4_RING_WAVES", 8);
+  return w == 16 ? 16 : 8;
+}
+
 static int occupancy_for(int bm, bool ring) {
-  static int cache[2][3] = {{-1, -1, -1}, {-1, -1, -1}};
+  static int cache[3][3] = {{-1, -1, -1}, {-1, -1, -1}, {-1, -1, -1}};
   const int bi = bm == 16 ? 0 : (bm == 32 ? 1 : 2);
-  int& c = cache[ring ? 1 : 0][bi];
+  const int rw = ring_waves();
+  int& c = cache[ring ? (rw == 16 ? 2 : 1) : 0][bi];
   if (c < 0) {
-    if (ring) {
-      c = bm == 16 ? occupancy_of(gemm_ring_kernel<16>, kRingThreads)
-                   : bm == 32 ? occupancy_of(gemm_ring_kernel<32>, kRingThreads)
-                              : occupancy_of(gemm_ring_kernel<64>, kRingThreads);
+    if (ring && rw == 16) {
+      c = bm == 16 ? occupancy_of(gemm_ring_kernel<16, 16>, 1024)
+                   : bm == 32 ? occupancy_of(gemm_ring_kernel<32, 16>, 1024)
+                              : occupancy_of(gemm_ring_kernel<64, 16>, 1024);
+    } else if (ring) {
+      c = bm == 16 ? occupancy_of(gemm_ring_kernel<16, 8>, 512)
+                   : bm == 32 ? occupancy_of(gemm_ring_kernel<32, 8>, 512)
+                              : occupancy_of(gemm_ring_kernel<64, 8>, 512);
     } else {
       c = bm == 16 ? occupancy_of(gemm_reg_kernel<16>, kRegThreads)
                    : bm == 32 ? occupancy_of(gemm_reg_kernel<32>, kRegThreads)
@@ -630,11 +718,6 @@ static int occupancy_for(int bm, bool ring) {
   return c;
 }
 
-static int env_int(const char* name, int dflt) {
-  const char* v = getenv(name);
-  if (!v || !*v) return dflt;
-  return atoi(v);
-}
 
 GemmPlan plan_gemm(int64_t rows, int64_t num_experts, int64_t n, int64_t k, bool grouped,
                    int cu_count) {
@@ -684,11 +767,16 @@ GemmPlan plan_gemm(int64_t rows, int64_t num_experts, int64_t n, int64_t k, bool
 
 hipError_t launch_gemm(const GemmPlan& pl, const GemmParams& p, hipStream_t stream) {
   dim3 grid(pl.grid);
-  if (pl.fast) {
-    dim3 block(kRingThreads);
-    if (pl.bm == 16) hipLaunchKernelGGL(gemm_ring_kernel<16>, grid, block, 0, stream, p);
-    else if (pl.bm == 32) hipLaunchKernelGGL(gemm_ring_kernel<32>, grid, block, 0, stream, p);
-    else hipLaunchKernelGGL(gemm_ring_kernel<64>, grid, block, 0, stream, p);
+  if (pl.fast && ring_waves() == 16) {
+    dim3 block(1024);
+    if (pl.bm == 16) hipLaunchKernelGGL((gemm_ring_kernel<16, 16>), grid, block, 0, stream, p);
+    else if (pl.bm == 32) hipLaunchKernelGGL((gemm_ring_kernel<32, 16>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((gemm_ring_kernel<64, 16>), grid, block, 0, stream, p);
+  } else if (pl.fast) {
+    dim3 block(512);
+    if (pl.bm == 16) hipLaunchKernelGGL((gemm_ring_kernel<16, 8>), grid, block, 0, stream, p);
+    else if (pl.bm == 32) hipLaunchKernelGGL((gemm_ring_kernel<32, 8>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((gemm_ring_kernel<64, 8>), grid, block, 0, stream, p);
   } else {
     dim3 block(kRegThreads);
     if (pl.bm == 16) hipLaunchKernelGGL(gemm_reg_kernel<16>, grid, block, 0, stream, p);

@@ -50,6 +50,13 @@ def parse():
                     help="skip the dense decode / 8192^3 / quantize side measurements")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time spent on the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run five 1 GiB device-to-device copies (run under rocprofv3 "
+                         "--pmc to calibrate FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV",
+                                                           "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="write profiles/traffic.json from rocprofv3 counter CSVs of a bench "
+                         "run and of --copy-calibration (no GPU needed)")
     return ap.parse_args()
 
 
@@ -229,8 +236,63 @@ def extras():
     return out
 
 
+COPY_BYTES = 1 << 30
+
+
+def copy_calibration():
+    import torch
+    a = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": COPY_BYTES, "copies": 5}), flush=True)
+
+
+def _counter_rows(path, counter):
+    import csv
+    return [(r["Kernel_Name"], float(r["Counter_Value"])) for r in csv.DictReader(open(path))
+            if r["Counter_Name"] == counter]
+
+
+def traffic_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
+    """HBM bytes per launch of each gemm kernel instantiation from rocprofv3
+    FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled by the ratio of
+    the known bytes of a 1 GiB copy to what the same counter reads for it."""
+    def copy_kib(path, counter):
+        vals = [v for n, v in _counter_rows(path, counter) if "copy" in n.lower() and v > 0]
+        return max(vals)
+    fetch_factor = COPY_BYTES / 1024.0 / copy_kib(copy_fetch_csv, "FETCH_SIZE")
+    write_factor = COPY_BYTES / 1024.0 / copy_kib(copy_write_csv, "WRITE_SIZE")
+    sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    out = {"_calibration": {"fetch_factor": fetch_factor, "write_factor": write_factor,
+                            "copy_bytes": COPY_BYTES}}
+    per = {}
+    for counter, path, factor in (("FETCH_SIZE", fetch_csv, fetch_factor),
+                                  ("WRITE_SIZE", write_csv, write_factor)):
+        for name, v in _counter_rows(path, counter):
+            if "gemm_ring_kernel" not in name and "gemm_reg_kernel" not in name:
+                continue
+            key = "nvfp4::" + name.split("nvfp4::", 1)[1].split("(")[0]
+            per.setdefault(key, {}).setdefault(counter, []).append(v * 1024.0 * factor)
+    for key, d in per.items():
+        fetch = sum(d.get("FETCH_SIZE", [0])) / max(1, len(d.get("FETCH_SIZE", [])))
+        write = sum(d.get("WRITE_SIZE", [0])) / max(1, len(d.get("WRITE_SIZE", [])))
+        out[key] = {"source_sha256": sha, "bytes_per_launch": fetch + write,
+                    "fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
+                    "dispatches": len(d.get("FETCH_SIZE", []))}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1, sort_keys=True)
+    print(json.dumps(out, indent=1, sort_keys=True))
+
+
 def main():
     args = parse()
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: every box here has a single MI355X, so "
               "--gpus %d is not supported (the sharding design is described in the docs)" %
@@ -240,6 +302,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     launches = build_workload()
     step_flops = sum(L["flops"] for L in launches)
     step_bytes = sum(L["bytes"] for L in launches)
@@ -275,7 +340,7 @@ def main():
         d["launches"] += 1
         d["names"].append(L["name"])
     bm, dom = max(by_bm.items(), key=lambda kv: kv[1]["ms"])
-    kernel = "nvfp4::gemm_ring_kernel<%d>" % bm
+    kernel = "nvfp4::gemm_ring_kernel<%d, 8>" % bm
     avg_ms = dom["ms"] / dom["launches"]
     bytes_per_launch = dom["bytes"] / dom["launches"]
     achieved = bytes_per_launch / (avg_ms * 1e-3) / 1e9

@@ -174,6 +174,18 @@ struct Unit {
   int e, ks, nt, tile, row0, row_end, k_beg, k_end;
 };
 
+// Work units are handed out in rounds of gridDim.x.  Within a round, unit
+// ids are placed XCD-major: the hardware dispatches workgroup w to XCD
+// w % 8, so consecutive unit ids -- the row tiles of one expert's weight
+// tile, then its other column tiles -- go to workgroups w, w+8, w+16, ... of
+// one XCD and stream the same weight bytes through that XCD's L2 at about
+// the same time instead of each fetching them from HBM.  The map is a
+// bijection of [0, G) onto itself, so every unit is processed exactly once.
+__device__ __forceinline__ int round_unit(int round, int w, int G) {
+  const int in_round = (G % 8 == 0) ? (w % 8) * (G / 8) + w / 8 : w;
+  return round * G + in_round;
+}
+
 template <int BM>
 __device__ __forceinline__ Unit decode_unit(const Sched& sc, const GemmParams& p, int unit) {
   // expert: last e with units[e] <= unit (empty experts have equal bounds)
@@ -452,7 +464,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_ring_kernel(GemmParams p) {
   const uint32_t ring0 = lds_addr(ring);
   const int q = lane >> 4;
 
-  for (int unit = blockIdx.x; unit < total; unit += gridDim.x) {
+  for (int round = 0; round * (int)gridDim.x < total; ++round) {
+    const int unit = round_unit(round, blockIdx.x, gridDim.x);
+    if (unit >= total) continue;
     const Unit u = decode_unit<BM>(sc, p, unit);
     const int n0 = u.nt * kBN;
     const u32x4_t rw =
@@ -609,7 +623,9 @@ __global__ __launch_bounds__(kRegThreads) void gemm_reg_kernel(GemmParams p) {
   const int total = build_schedule<kRegThreads, BM>(sc, p);
   const int N = p.n, K = p.k;
 
-  for (int unit = blockIdx.x; unit < total; unit += gridDim.x) {
+  for (int round = 0; round * (int)gridDim.x < total; ++round) {
+    const int unit = round_unit(round, blockIdx.x, gridDim.x);
+    if (unit >= total) continue;
     const Unit u = decode_unit<BM>(sc, p, unit);
     const __amdgpu_buffer_rsrc_t rw =
         make_rsrc(p.w + (int64_t)u.e * N * (K / 2), (uint32_t)N * (uint32_t)(K / 2));

@@ -122,6 +122,17 @@ def bm_for(rows, experts):
     return bm
 
 
+def kernel_for(bm):
+    # mirrors the library's kernel configuration for K % 64 == 0: 4-wave
+    # workgroups on 128-column tiles up to 32 rows, 8 waves on 256 columns
+    # for 64-row tiles (template arguments: rows, ring slots, waves, columns)
+    if bm == 16:
+        return "nvfp4::gemm_kp_kernel<16, 5, 4, 128>"
+    if bm == 32:
+        return "nvfp4::gemm_kp_kernel<32, 4, 4, 128>"
+    return "nvfp4::gemm_kp_kernel<64, 4, 8, 256>"
+
+
 def run_launch(L):
     import block_scaled_fp4_nibble_amd as nv
     nv.grouped_gemm(L["x"], L["off"], L["qw"], out=L["y"])
@@ -272,7 +283,7 @@ def traffic_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
     for counter, path, factor in (("FETCH_SIZE", fetch_csv, fetch_factor),
                                   ("WRITE_SIZE", write_csv, write_factor)):
         for name, v in _counter_rows(path, counter):
-            if "gemm_ring_kernel" not in name and "gemm_reg_kernel" not in name:
+            if "gemm_kp_kernel" not in name and "gemm_reg_kernel" not in name:
                 continue
             key = "nvfp4::" + name.split("nvfp4::", 1)[1].split("(")[0]
             per.setdefault(key, {}).setdefault(counter, []).append(v * 1024.0 * factor)
@@ -340,7 +351,7 @@ def main():
         d["launches"] += 1
         d["names"].append(L["name"])
     bm, dom = max(by_bm.items(), key=lambda kv: kv[1]["ms"])
-    kernel = "nvfp4::gemm_ring_kernel<%d, 8>" % bm
+    kernel = kernel_for(bm)
     avg_ms = dom["ms"] / dom["launches"]
     bytes_per_launch = dom["bytes"] / dom["launches"]
     achieved = bytes_per_launch / (avg_ms * 1e-3) / 1e9

@@ -18,28 +18,26 @@
 //
 // gfx950 design
 //  - One persistent grid.  A work unit is (expert, row tile of BM rows,
-//    column tile of 256 weight rows, K split).  Every workgroup reads the
+//    column tile of BN weight rows, K split).  Every workgroup reads the
 //    expert offsets from device memory, builds the per-expert unit prefix in
-//    LDS and walks units blockIdx.x, +gridDim.x, ...  Empty experts own no
-//    units.  There is no host synchronization and no inter-workgroup wait.
+//    LDS and walks units in XCD-aware rounds.  Empty experts own no units.
+//    There is no host synchronization and no inter-workgroup wait.
 //  - MFMA v_mfma_f32_16x16x32_bf16.  Operand A = activations (16 rows),
 //    operand B = dequantized weights (16 weight rows = 16 output columns).
 //    Lane l holds row/column l % 16 and 8 consecutive K of lane group
 //    q = l / 16; which real K a slot carries is a free choice as long as A and
 //    B agree, and it is chosen so that each lane's weight bytes are
-//    contiguous.
+//    contiguous and its 16 K share one block scale.
 //  - Dequant: a nibble pair becomes two exact FP32 values with the gfx950 FP4
 //    conversion (scale 1.0; the instruction would apply only the exponent of
 //    a scale), is multiplied by the decoded E4M3 block scale (exact), and the
 //    upper halves form two BF16 values.  The global scale g is applied once
 //    to the FP32 accumulator in the epilogue.
-//  - Ring kernel (k % 64 == 0): 8 waves, each owning 32 of the 256 columns.
-//    K advances in 128-wide stages held in a 4-deep LDS ring: packed weights
-//    (256 rows x 64 B), block scales (256 x 8 B) and the activation tile
-//    (BM x 256 B), all written by buffer_load ... lds (no register staging),
-//    three stages in flight while the fourth is multiplied out.  Rows of the
-//    staged tiles are XOR-swizzled in 16-byte units so the 16-byte fragment
-//    reads of 16 lanes spread over all LDS bank groups.
+//  - K-phase kernel (k % 64 == 0): weights, activations and scales stream
+//    through an LDS ring filled by buffer_load ... lds; each wave owns a
+//    column slice and one K half of every stage; row fragments that hold
+//    only padding rows of a tile are skipped (the K loop is instantiated per
+//    number of occupied fragments).  Details at the kernel.
 //  - Register kernel (any k % 16 == 0): 4 waves x 64 columns, weights loaded
 //    straight into registers one 256-wide chunk ahead, activations staged
 //    through a double-buffered LDS tile.
@@ -117,15 +115,17 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total)
   return base + incl - v;
 }
 
-// Per-workgroup schedule: expert segments and exclusive prefixes of work
-// units and output tiles per expert.
+// Per-workgroup schedule: exclusive prefix of work units per expert (the
+// expert segments themselves are read from the offsets in device memory).
 struct Sched {
-  int off[kMaxExperts + 1];
   int units[kMaxExperts + 1];
-  int tiles[kMaxExperts + 1];
   int tmp[16];
   int flag;
 };
+
+__device__ __forceinline__ int seg_begin(const GemmParams& p, int e) {
+  return p.offsets ? p.offsets[e] : (e == 0 ? 0 : (int)p.rows);
+}
 
 // Fills `sc`; returns the total unit count, or -1 (after flagging the status
 // word) when the offsets are malformed.
@@ -133,39 +133,27 @@ template <int THREADS, int BM>
 __device__ int build_schedule(Sched& sc, const GemmParams& p) {
   const int tid = threadIdx.x;
   const int E = p.num_experts;
-  for (int e = tid; e <= E; e += THREADS)
-    sc.off[e] = p.offsets ? p.offsets[e] : (e == 0 ? 0 : (int)p.rows);
-  __syncthreads();
-  int bad = 0;
-  for (int e = tid; e < E; e += THREADS) bad |= (sc.off[e + 1] < sc.off[e]);
-  if (tid == 0) bad |= (sc.off[0] != 0) | ((int64_t)sc.off[E] != p.rows);
+  constexpr int PER = (kMaxExperts + THREADS - 1) / THREADS;  // experts per thread
+  int bad = 0, my_units = 0;
+  for (int e = PER * tid; e < PER * tid + PER && e < E; ++e) {
+    const int a = seg_begin(p, e), b = seg_begin(p, e + 1);
+    bad |= b < a;
+    my_units += (b - a + BM - 1) / BM * p.n_tiles * p.splits;
+  }
+  if (tid == 0) bad |= (seg_begin(p, 0) != 0) | ((int64_t)seg_begin(p, E) != p.rows);
   bad = __syncthreads_or(bad);
   if (bad) {
     if (blockIdx.x == 0 && tid == 0 && p.d_status != nullptr)
       atomicOr(p.d_status, NVFP4_DSTATUS_BAD_OFFSETS);
     return -1;
   }
-  constexpr int PER = (kMaxExperts + THREADS - 1) / THREADS;  // experts per thread
-  int my_units = 0, my_tiles = 0;
-  for (int e = PER * tid; e < PER * tid + PER && e < E; ++e) {
-    const int mt = (sc.off[e + 1] - sc.off[e] + BM - 1) / BM;
-    my_tiles += mt * p.n_tiles;
-    my_units += mt * p.n_tiles * p.splits;
-  }
-  int total_units, total_tiles;
+  int total_units;
   int ubase = block_exclusive_scan<THREADS>(my_units, sc.tmp, &total_units);
-  int tbase = block_exclusive_scan<THREADS>(my_tiles, sc.tmp, &total_tiles);
   for (int e = PER * tid; e < PER * tid + PER && e < E; ++e) {
     sc.units[e] = ubase;
-    sc.tiles[e] = tbase;
-    const int mt = (sc.off[e + 1] - sc.off[e] + BM - 1) / BM;
-    ubase += mt * p.n_tiles * p.splits;
-    tbase += mt * p.n_tiles;
+    ubase += (seg_begin(p, e + 1) - seg_begin(p, e) + BM - 1) / BM * p.n_tiles * p.splits;
   }
-  if (tid == 0) {
-    sc.units[E] = total_units;
-    sc.tiles[E] = total_tiles;
-  }
+  if (tid == 0) sc.units[E] = total_units;
   __syncthreads();
   return total_units;
 }
@@ -186,6 +174,8 @@ __device__ __forceinline__ int round_unit(int round, int w, int G) {
   return round * G + in_round;
 }
 
+// Units of expert e are ordered (column tile, split, row tile); the expert's
+// output tiles (for the split-K counters) are numbered units / splits.
 template <int BM>
 __device__ __forceinline__ Unit decode_unit(const Sched& sc, const GemmParams& p, int unit) {
   // expert: last e with units[e] <= unit (empty experts have equal bounds)
@@ -195,15 +185,16 @@ __device__ __forceinline__ Unit decode_unit(const Sched& sc, const GemmParams& p
     if (sc.units[mid] <= unit) lo = mid; else hi = mid;
   }
   Unit u;
-  u.e = lo;
-  const int seg0 = sc.off[lo], seg1 = sc.off[lo + 1];
+  u.e = __builtin_amdgcn_readfirstlane(lo);
+  const int seg0 = __builtin_amdgcn_readfirstlane(seg_begin(p, u.e));
+  const int seg1 = __builtin_amdgcn_readfirstlane(seg_begin(p, u.e + 1));
   const int mtiles = (seg1 - seg0 + BM - 1) / BM;
-  const int local = unit - sc.units[lo];
+  const int local = unit - sc.units[u.e];
   const int mt = local % mtiles;
   const int rest = local / mtiles;
   u.ks = rest % p.splits;
   u.nt = rest / p.splits;
-  u.tile = sc.tiles[lo] + u.nt * mtiles + mt;
+  u.tile = sc.units[u.e] / p.splits + u.nt * mtiles + mt;
   u.row0 = seg0 + mt * BM;
   u.row_end = min(u.row0 + BM, seg1);
   u.k_beg = u.ks * p.k_split;
@@ -211,23 +202,24 @@ __device__ __forceinline__ Unit decode_unit(const Sched& sc, const GemmParams& p
   return u;
 }
 
-// Split-K hand-off and epilogue for a workgroup of WAVES waves, each holding
-// NF x NW MFMA accumulator tiles (column = nt*256 + wave*NW*16 + j*16 + l%16,
-// row = row0 + f*16 + 4*(l/16) + r).  Returns false when another split of
-// the tile will finish it.
-template <int NF, int NW, int WAVES>
+// Split-K hand-off and epilogue for a workgroup of WAVES waves over a BN-wide
+// column tile, each wave holding NF x NW MFMA accumulator tiles
+// (column = nt*BN + wave*NW*16 + j*16 + l%16, row = row0 + f*16 + 4*(l/16) + r).
+// Returns false when another split of the tile will finish it.
+template <int NF, int NW, int WAVES, int BN>
 __device__ __forceinline__ bool finish_tile(f32x4_t (&acc)[NF][NW], const GemmParams& p,
                                             const Unit& u, Sched& sc) {
   constexpr int BM = NF * 16;
+  static_assert(WAVES * NW * 16 == BN, "waves cover the column tile");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = p.splits;
   if (S > 1) {
-    float* part = p.partials + (int64_t)u.tile * S * (BM * kBN);
+    float* part = p.partials + (int64_t)u.tile * S * (BM * BN);
 #pragma unroll
     for (int f = 0; f < NF; ++f)
 #pragma unroll
       for (int j = 0; j < NW; ++j)
-        *reinterpret_cast<f32x4_t*>(part + (int64_t)u.ks * (BM * kBN) +
+        *reinterpret_cast<f32x4_t*>(part + (int64_t)u.ks * (BM * BN) +
                                     (((wave * NF + f) * NW + j) * kWave + lane) * 4) = acc[f][j];
     fence_release_agent();
     __syncthreads();
@@ -246,7 +238,7 @@ __device__ __forceinline__ bool finish_tile(f32x4_t (&acc)[NF][NW], const GemmPa
         for (int s = 0; s < S; ++s) {
           f32x4_t v = (s == u.ks) ? acc[f][j]
                                   : __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(
-                                        part + (int64_t)s * (BM * kBN) +
+                                        part + (int64_t)s * (BM * BN) +
                                         (((wave * NF + f) * NW + j) * kWave + lane) * 4));
           sum = (s == 0) ? v : sum + v;
         }
@@ -260,7 +252,7 @@ __device__ __forceinline__ bool finish_tile(f32x4_t (&acc)[NF][NW], const GemmPa
   for (int f = 0; f < NF; ++f)
 #pragma unroll
     for (int j = 0; j < NW; ++j) {
-      const int col = u.nt * kBN + wave * (NW * 16) + j * 16 + r16;
+      const int col = u.nt * BN + wave * (NW * 16) + j * 16 + r16;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = u.row0 + f * 16 + 4 * q + r;
@@ -277,31 +269,9 @@ __device__ __forceinline__ bool finish_tile(f32x4_t (&acc)[NF][NW], const GemmPa
   return true;
 }
 
-// ---- ring kernel (k % 64 == 0) ------------------------------------------------
+// ---- staged-ring pieces (k % 64 == 0) ---------------------------------------------
 
-// A ring workgroup has WAVES = 8 or 16 waves; each owns 256 / WAVES of the
-// unit's columns, i.e. NW = 16 / WAVES MFMA column tiles.
 constexpr int kRingKC = 128;       // K per stage
-constexpr int kRingStages = 4;
-
-template <int BM, int WAVES>
-struct RingLayout {
-  static constexpr int kNW = 16 / WAVES;            // MFMA column tiles per wave
-  static constexpr int kWPerWave = 16 / WAVES;      // 1 KB weight loads per wave per stage
-  static constexpr int kW = 0;                      // 256 rows x 64 B packed nibbles
-  static constexpr int kX = kW + kBN * 64;          // BM rows x 256 B activations
-  static constexpr int kStage = kX + BM * 256;
-  static constexpr int kXInstr = BM / 4;            // 1 KB (4-row) loads per stage
-  static constexpr int kXPerWave = kXInstr >= WAVES ? kXInstr / WAVES : 1;
-  static constexpr int kLoadsPerStage = kWPerWave + kXPerWave;  // per wave
-  // Block scales arrive in windows of 4 stages (512 K = 32 bytes per row), two
-  // window slots: one 1 KB load per wave per window instead of 8-byte row
-  // pieces every stage.
-  static constexpr int kWinStages = 4;
-  static constexpr int kWinBytes = kBN * 32;
-  static constexpr int kSWin = kRingStages * kStage;
-  static constexpr int kTotal = kSWin + 2 * kWinBytes;
-};
 
 // s_waitcnt vmcnt(n) for a run-time n in [0, 15]: the immediate must be a
 // constant.  Encoding (gfx9): vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits
@@ -318,203 +288,308 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 #undef NVFP4_VMCNT
 }
 
-// Per-lane constant parts of a unit's load offsets (the K position of a
-// stage goes into the instruction's scalar offset).
-template <int BM, int WAVES>
-struct RingOffsets {
-  uint32_t w[16 / WAVES];                           // weight pieces
-  uint32_t x[RingLayout<BM, WAVES>::kXPerWave];     // activation pieces
-  int xk[RingLayout<BM, WAVES>::kXPerWave];         // K of the piece within a stage
-  uint32_t s;                                       // scale window piece
+// ---- K-phase kernel (k % 64 == 0) ----------------------------------------------
+//
+// A work unit is (expert, row tile of BM rows, column tile of BN = 128 or 256
+// weight rows, K split).  K advances in 128-wide stages held in an
+// NSLOT-deep LDS ring: packed weights (BN rows x 64 B), the activation tile
+// (BM rows x 256 B), and block scales in windows of 4 stages (BN rows x
+// 32 B), all written by buffer_load ... lds (no register staging).
+//
+// The KW waves split the work as wave w = 2 ch + kp: it owns the
+// CPW = 2 BN / KW columns [CPW ch, CPW ch + CPW) and the K half
+// [64 kp, 64 kp + 64) of every stage.  Each wave thus reads only half of the
+// staged activation tile, and its column tiles share every activation
+// fragment; the two K halves of a column are summed through LDS once per
+// unit.  Operands of stage c + 1 are read from LDS into registers while stage
+// c is multiplied out, so LDS latency hides behind a whole stage of
+// dequantization and MFMA; NSLOT - 2 stages are in flight from HBM meanwhile.
+//
+// Small tiles run as 4-wave workgroups on 128 columns, two workgroups per
+// CU: the two waves that share a SIMD then belong to different workgroups,
+// so the SIMD's issue arbitration (which favours the older wave) never makes
+// one of them wait for the other at a barrier.
+//
+// LDS swizzles (chosen for gfx950's ds_read_b128 / ds_read_b64 bank mapping):
+// activation row r keeps its 16-byte chunk c in slot c ^ (r & 15); weight row
+// R keeps its 16-byte chunk c in slot c ^ ((R >> 2) & 3).
+template <int BM, int NSLOT, int KW, int BN>
+struct KpLayout {
+  static constexpr int kCPW = 2 * BN / KW;          // columns per wave
+  static constexpr int kNJ = kCPW / 16;             // MFMA column tiles per wave
+  static constexpr int kW = 0;                      // BN rows x 64 B packed nibbles
+  static constexpr int kX = BN * 64;                // BM rows x 256 B activations
+  static constexpr int kStage = kX + BM * 256;
+  static constexpr int kWPerWave = BN / 16 / KW;    // 1 KB (16-row) weight loads per wave
+  static constexpr int kXInstr = BM / 4;            // 1 KB (4-row) activation loads
+  static constexpr int kXPerWave = kXInstr >= KW ? kXInstr / KW : 1;
+  static constexpr int kSInstr = BN / 32;           // 1 KB (32-row) scale window loads
+  static constexpr int kLoadsPerStage = kWPerWave + kXPerWave;
+  static constexpr int kWinStages = 4;              // scale window = 4 stages = 512 K
+  static constexpr int kWinBytes = BN * 32;
+  static constexpr int kSWin = NSLOT * kStage;
+  static constexpr int kTotal = kSWin + 2 * kWinBytes;
+  static_assert(kWPerWave >= 1 && KW >= kSInstr, "load split");
+  static_assert(kNJ % 2 == 0, "column tiles split between the K halves");
+  static_assert(NSLOT >= 3 && NSLOT <= 5, "windows are issued one window ahead");
+  static_assert(kTotal + (int)sizeof(Sched) <= 160 * 1024, "LDS budget");
+  static_assert(kTotal >= KW * (BM / 16) * (kNJ / 2) * 1024, "reduction buffer fits the ring");
 };
 
-template <int BM, int WAVES>
-__device__ __forceinline__ RingOffsets<BM, WAVES> ring_offsets(int n0, int K, int wave,
-                                                               int lane) {
-  using L = RingLayout<BM, WAVES>;
-  RingOffsets<BM, WAVES> o;
-  // weights: load t covers rows 16t..16t+15, 64 B each; slot s of row R holds
-  // the row's 16-byte piece s ^ ((R >> 1) & 3)
+template <int BM, int KW, int BN>
+struct KpOffsets {
+  uint32_t w[KpLayout<BM, 4, KW, BN>::kWPerWave];
+  uint32_t x[KpLayout<BM, 4, KW, BN>::kXPerWave];
+  int xk[KpLayout<BM, 4, KW, BN>::kXPerWave];
+  uint32_t s;
+};
+
+template <int BM, int KW, int BN>
+__device__ __forceinline__ KpOffsets<BM, KW, BN> kp_offsets(int n0, int K, int wave, int lane) {
+  using L = KpLayout<BM, 4, KW, BN>;
+  KpOffsets<BM, KW, BN> o;
+  // weights: load t covers rows 16t..16t+15 (64 B each); slot s of row R
+  // receives chunk s ^ ((R >> 2) & 3)
 #pragma unroll
   for (int tt = 0; tt < L::kWPerWave; ++tt) {
-    const int t = wave * L::kWPerWave + tt;
-    const int R = t * 16 + (lane >> 2);
-    const int g = (lane & 3) ^ ((R >> 1) & 3);
+    const int R = (wave * L::kWPerWave + tt) * 16 + (lane >> 2);
+    const int g = (lane & 3) ^ ((R >> 2) & 3);
     o.w[tt] = (uint32_t)(n0 + R) * (uint32_t)(K / 2) + (uint32_t)(16 * g);
   }
-  // activations: load t covers rows 4t..4t+3, 256 B each; slot s of row r
-  // holds piece s ^ (r & 7).  With fewer loads than waves, waves repeat a
-  // load (same bytes to the same place) so every wave issues the same count.
+  // activations: load t covers rows 4t..4t+3 (256 B each); slot s of row r
+  // receives chunk s ^ (r & 15).  With fewer loads than waves, waves repeat
+  // a load (same bytes to the same place) so every wave issues the same count.
 #pragma unroll
   for (int tt = 0; tt < L::kXPerWave; ++tt) {
-    const int t = L::kXInstr >= WAVES ? wave * L::kXPerWave + tt : wave % L::kXInstr;
+    const int t = L::kXInstr >= KW ? wave * L::kXPerWave + tt : wave % L::kXInstr;
     const int r = t * 4 + (lane >> 4);
-    const int g = (lane & 15) ^ (r & 7);
+    const int g = (lane & 15) ^ (r & 15);
     o.x[tt] = (uint32_t)r * (uint32_t)(K * 2) + (uint32_t)(16 * g);
     o.xk[tt] = 8 * g;
   }
-  // scale window: eight 1 KB loads of 32 rows x 32 bytes; with 16 waves,
-  // waves 8-15 repeat the loads of waves 0-7
+  // scale window: 1 KB loads of 32 rows x 32 bytes, one per wave (waves
+  // beyond the load count repeat a load)
   {
-    const int R = (wave & 7) * 32 + (lane >> 1);
+    const int R = (wave % L::kSInstr) * 32 + (lane >> 1);
     o.s = (uint32_t)(n0 + R) * (uint32_t)(K / 16) + (uint32_t)(16 * (lane & 1));
   }
   return o;
 }
 
-// Issue one stage (K range [kc, kc + 128) of the unit) into LDS.  Weight
-// pieces past the split end are loaded anyway (their block scales are taken
-// as 0 when multiplied); activation pieces past it read as zero.
-template <int BM, int WAVES>
-__device__ __forceinline__ void ring_issue(uint32_t stage, u32x4_t rw, u32x4_t rx,
-                                           const RingOffsets<BM, WAVES>& o, int K, int kc,
-                                           int k_end, int wave) {
-  using L = RingLayout<BM, WAVES>;
+template <int BM, int NSLOT, int KW, int BN>
+__device__ __forceinline__ void kp_issue(uint32_t stage, u32x4_t rw, u32x4_t rx,
+                                         const KpOffsets<BM, KW, BN>& o, int kc, int k_end,
+                                         int wave) {
+  using L = KpLayout<BM, NSLOT, KW, BN>;
 #pragma unroll
   for (int tt = 0; tt < L::kWPerWave; ++tt)
     lds_dma16(stage + L::kW + (wave * L::kWPerWave + tt) * 1024, o.w[tt], (uint32_t)(kc / 2), rw);
   const bool tail = kc + kRingKC > k_end;
 #pragma unroll
   for (int tt = 0; tt < L::kXPerWave; ++tt) {
-    const int t = L::kXInstr >= WAVES ? wave * L::kXPerWave + tt : wave % L::kXInstr;
+    const int t = L::kXInstr >= KW ? wave * L::kXPerWave + tt : wave % L::kXInstr;
     const uint32_t voff = (tail && kc + o.xk[tt] >= k_end) ? kOffNone : o.x[tt];
     lds_dma16(stage + L::kX + t * 1024, voff, (uint32_t)(kc * 2), rx);
   }
 }
 
 // Issue the scale window [kw, kw + 512) of the unit (one 1 KB load per wave).
-__device__ __forceinline__ void ring_issue_scales(uint32_t slot, u32x4_t rs, uint32_t soff_lane,
-                                                  int kw, int wave) {
-  lds_dma16(slot + (wave & 7) * 1024, soff_lane, (uint32_t)(kw / 16), rs);
+template <int BM, int NSLOT, int KW, int BN>
+__device__ __forceinline__ void kp_issue_scales(uint32_t slot, u32x4_t rs, uint32_t soff_lane,
+                                                int kw, int wave) {
+  using L = KpLayout<BM, NSLOT, KW, BN>;
+  lds_dma16(slot + (wave % L::kSInstr) * 1024, soff_lane, (uint32_t)(kw / 16), rs);
 }
 
-// One stage's operands, read from LDS into registers one iteration ahead.
-template <int BM, int WAVES>
-struct StageRegs {
-  u32x4_t wd[16 / WAVES];
-  uint32_t s2[16 / WAVES];
-  bf16x8_t a[4][BM / 16];
+// One stage's operands of one wave: per column tile j, 16 nibbles (two MFMA
+// K steps) and one E4M3 block scale; per K step i and row tile f, one
+// activation fragment.
+template <int BM, int NJ>
+struct KpRegs {
+  u32x2_t wd[NJ];
+  uint32_t sc[NJ];
+  bf16x8_t a[2][BM / 16];
 };
 
-// Lane group q supplies K = kc + 32q + 8i .. +7 in MFMA step i; its two block
-// scales sit at byte 8 * (stage index within the window) + 2q of the row's
-// window entry.  Scales of K slots past the split end are taken as 0 (their
-// weight nibbles may belong to the next split).
-template <int BM, int WAVES>
-__device__ __forceinline__ void ring_read(StageRegs<BM, WAVES>& r, const uint8_t* stage,
-                                          const uint8_t* swin, int sub, bool kvalid, int wave,
-                                          int lane) {
-  using L = RingLayout<BM, WAVES>;
-  constexpr int NF = BM / 16;
+// Lane group q of wave half kp supplies K = 64 kp + 16 q + 8 i .. +7 of the
+// stage in MFMA step i: its 16 K are one scale block (block 4 kp + q of the
+// stage), 8 contiguous weight bytes and two 16-byte activation chunks.
+template <int BM, int NJ, int NFE, int BN>
+__device__ __forceinline__ void kp_read(KpRegs<BM, NJ>& r, const uint8_t* stage,
+                                        const uint8_t* swin, int sub, bool kvalid, int kp,
+                                        int ch, int lane) {
   const int q = lane >> 4, r16 = lane & 15;
+  const int cw = 2 * kp + (q >> 1);
 #pragma unroll
-  for (int j = 0; j < L::kNW; ++j) {
-    const int R = wave * (L::kNW * 16) + j * 16 + r16;
-    r.wd[j] = *reinterpret_cast<const u32x4_t*>(stage + L::kW + R * 64 + 16 * (q ^ ((R >> 1) & 3)));
-    const uint32_t s2 = *reinterpret_cast<const uint16_t*>(swin + R * 32 + 8 * sub + 2 * q);
-    r.s2[j] = kvalid ? s2 : 0u;
+  for (int j = 0; j < NJ; ++j) {
+    const int R = ch * (NJ * 16) + j * 16 + r16;
+    r.wd[j] = *reinterpret_cast<const u32x2_t*>(stage + R * 64 + 16 * (cw ^ ((R >> 2) & 3)) +
+                                                8 * (q & 1));
+    const uint32_t s = swin[R * 32 + 8 * sub + 4 * kp + q];
+    r.sc[j] = kvalid ? s : 0u;
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int f = 0; f < NF; ++f)
-      r.a[i][f] = *reinterpret_cast<const bf16x8_t*>(stage + L::kX + (f * 16 + r16) * 256 +
-                                                     16 * ((4 * q + i) ^ (r16 & 7)));
+    for (int f = 0; f < NFE; ++f)
+      r.a[i][f] = *reinterpret_cast<const bf16x8_t*>(stage + BN * 64 + (f * 16 + r16) * 256 +
+                                                     16 * ((8 * kp + 2 * q + i) ^ r16));
 }
 
-// Multiply out one stage held in registers: 4 MFMA steps of 32 K slots.
-template <int BM, int WAVES>
-__device__ __forceinline__ void ring_mma(f32x4_t (&acc)[BM / 16][16 / WAVES],
-                                         const StageRegs<BM, WAVES>& r) {
-  constexpr int NF = BM / 16, NW = 16 / WAVES;
-  float scl[NW][2];
+template <int BM, int NJ, int NFE>
+__device__ __forceinline__ void kp_mma(f32x4_t (&acc)[BM / 16][NJ], const KpRegs<BM, NJ>& r) {
+  float scl[NJ];
 #pragma unroll
-  for (int j = 0; j < NW; ++j) {
-    scl[j][0] = decode_e4m3<0>(r.s2[j]);
-    scl[j][1] = decode_e4m3<1>(r.s2[j]);
-  }
+  for (int j = 0; j < NJ; ++j) scl[j] = decode_e4m3<0>(r.sc[j]);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < NW; ++j) {
-      const bf16x8_t b = dequant8(r.wd[j][i], scl[j][i >> 1]);
+    for (int j = 0; j < NJ; ++j) {
+      const bf16x8_t b = dequant8(r.wd[j][i], scl[j]);
 #pragma unroll
-      for (int f = 0; f < NF; ++f)
+      for (int f = 0; f < NFE; ++f)
         acc[f][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.a[i][f], b, acc[f][j], 0, 0, 0);
     }
 }
 
-// Pipeline per unit (per wave, in issue order): scale window 0, stages
-// 0..2; then iteration c waits for stage c, passes the barrier, issues stage
-// c+3 into the slot of stage c-1 plus, when c % 4 == 0, scale window c/4 + 1,
-// and multiplies out stage c (three stages in flight meanwhile).
-template <int BM, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void gemm_ring_kernel(GemmParams p) {
-  using L = RingLayout<BM, WAVES>;
-  constexpr int NF = BM / 16;
-  constexpr int NW = L::kNW;
+// The K loop of one unit, for tiles whose rows fill NFE of the BM / 16 row
+// fragments (fragments past NFE are pure padding and are skipped).
+//
+// Per unit (per wave, in issue order): scale window 0, stages 0..D-1
+// (D = NSLOT - 1).  Iteration c waits until stage c + 1 has landed, passes the
+// barrier (every wave is then done with stage c - 1, whose slot is refilled),
+// issues scale window c/4 + 1 when c % 4 == 0 and stage c + D, reads stage
+// c + 1 into registers and multiplies out stage c.
+template <int BM, int NSLOT, int KW, int BN, int NFE>
+__device__ __forceinline__ void kp_kloop(f32x4_t (&acc)[BM / 16][2 * BN / KW / 16],
+                                         uint8_t* ring, const Unit& u, u32x4_t rw, u32x4_t rs,
+                                         u32x4_t rx, const KpOffsets<BM, KW, BN>& off, int kp,
+                                         int ch, int wave, int lane) {
+  using L = KpLayout<BM, NSLOT, KW, BN>;
+  constexpr int NJ = L::kNJ;
+  constexpr int D = NSLOT - 1;
   constexpr int WS = L::kWinStages;
   constexpr int LS = L::kLoadsPerStage;
+  const int q = lane >> 4;
+  const uint32_t ring0 = lds_addr(ring);
+  const int nch = (u.k_end - u.k_beg + kRingKC - 1) / kRingKC;
+  const int nwin = (nch + WS - 1) / WS;
+  // K validity of this lane's scale block in stage c
+  auto kvalid = [&](int c) { return u.k_beg + c * kRingKC + 64 * kp + 16 * q < u.k_end; };
+  kp_issue_scales<BM, NSLOT, KW, BN>(ring0 + L::kSWin, rs, off.s, u.k_beg, wave);
+  for (int s = 0; s < D && s < nch; ++s)
+    kp_issue<BM, NSLOT, KW, BN>(ring0 + s * L::kStage, rw, rx, off, u.k_beg + s * kRingKC,
+                                u.k_end, wave);
+  wait_vmcnt(LS * (min(D - 1, nch - 1)));
+  __syncthreads();
+  KpRegs<BM, NJ> ra, rb;
+  kp_read<BM, NJ, NFE, BN>(ra, ring, ring + L::kSWin, 0, kvalid(0), kp, ch, lane);
+
+  auto step = [&](int c, const KpRegs<BM, NJ>& cur, KpRegs<BM, NJ>& nxt) {
+    if (c + 1 < nch) {
+      // loads issued after stage c + 1: stages c+2 .. c+D-1 and the windows
+      // issued at iterations c+2-D .. c-1
+      int after = LS * max(0, min(c + D - 1, nch - 1) - (c + 1));
+      for (int i = max(0, c + 2 - D); i < c; ++i)
+        after += (i % WS == 0 && i / WS + 1 < nwin) ? 1 : 0;
+      wait_vmcnt(after);
+      __syncthreads();
+      if (c % WS == 0 && c / WS + 1 < nwin)
+        kp_issue_scales<BM, NSLOT, KW, BN>(ring0 + L::kSWin + ((c / WS + 1) & 1) * L::kWinBytes,
+                                           rs, off.s, u.k_beg + (c / WS + 1) * WS * kRingKC, wave);
+      if (c + D < nch)
+        kp_issue<BM, NSLOT, KW, BN>(ring0 + ((c + D) % NSLOT) * L::kStage, rw, rx, off,
+                                    u.k_beg + (c + D) * kRingKC, u.k_end, wave);
+      kp_read<BM, NJ, NFE, BN>(nxt, ring + ((c + 1) % NSLOT) * L::kStage,
+                               ring + L::kSWin + (((c + 1) / WS) & 1) * L::kWinBytes,
+                               (c + 1) % WS, kvalid(c + 1), kp, ch, lane);
+    }
+    kp_mma<BM, NJ, NFE>(acc, cur);
+  };
+  for (int c = 0; c < nch; c += 2) {
+    step(c, ra, rb);
+    if (c + 1 < nch) step(c + 1, rb, ra);
+  }
+}
+
+template <int BM, int NSLOT, int KW, int BN>
+__global__ __launch_bounds__(KW * 64) void gemm_kp_kernel(GemmParams p) {
+  using L = KpLayout<BM, NSLOT, KW, BN>;
+  constexpr int NF = BM / 16;
+  constexpr int NJ = L::kNJ;
+  constexpr int NH = NJ / 2;  // column tiles a wave keeps after the K-half exchange
   __shared__ __attribute__((aligned(16))) uint8_t ring[L::kTotal];
   __shared__ Sched sc;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int total = build_schedule<WAVES * 64, BM>(sc, p);
+  const int kp = wave & 1, ch = wave >> 1;
+  const int total = build_schedule<KW * 64, BM>(sc, p);
   const int N = p.n, K = p.k;
-  const uint32_t ring0 = lds_addr(ring);
-  const int q = lane >> 4;
 
   for (int round = 0; round * (int)gridDim.x < total; ++round) {
     const int unit = round_unit(round, blockIdx.x, gridDim.x);
     if (unit >= total) continue;
     const Unit u = decode_unit<BM>(sc, p, unit);
-    const int n0 = u.nt * kBN;
+    const int n0 = u.nt * BN;
     const u32x4_t rw =
         rsrc_words(p.w + (int64_t)u.e * N * (K / 2), (uint32_t)N * (uint32_t)(K / 2));
     const u32x4_t rs =
         rsrc_words(p.s + (int64_t)u.e * N * (K / 16), (uint32_t)N * (uint32_t)(K / 16));
     const u32x4_t rx =
         rsrc_words(p.x + (int64_t)u.row0 * K, (uint32_t)(u.row_end - u.row0) * (uint32_t)(K * 2));
-    const RingOffsets<BM, WAVES> off = ring_offsets<BM, WAVES>(n0, K, wave, lane);
+    const KpOffsets<BM, KW, BN> off = kp_offsets<BM, KW, BN>(n0, K, wave, lane);
+    // 16-row fragments holding rows of this tile (the rest is padding)
+    const int nf = min(NF, (u.row_end - u.row0 + 15) / 16);
 
-    f32x4_t acc[NF][NW];
+    f32x4_t acc[NF][NJ];
 #pragma unroll
     for (int f = 0; f < NF; ++f)
 #pragma unroll
-      for (int j = 0; j < NW; ++j) acc[f][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < NJ; ++j) acc[f][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    const int nch = (u.k_end - u.k_beg + kRingKC - 1) / kRingKC;
-    const int nwin = (nch + WS - 1) / WS;
-    ring_issue_scales(ring0 + L::kSWin, rs, off.s, u.k_beg, wave);
-    for (int s = 0; s < kRingStages - 1 && s < nch; ++s)
-      ring_issue<BM, WAVES>(ring0 + s * L::kStage, rw, rx, off, K, u.k_beg + s * kRingKC,
-                            u.k_end, wave);
-    for (int c = 0; c < nch; ++c) {
-      // Loads this wave issued after stage c: the (up to two) later stages,
-      // plus any window issued at iterations c-3 .. c-1.  Waiting until only
-      // those are outstanding means stage c (and the window it reads, issued
-      // earlier) has landed; the barrier extends that to every wave's loads
-      // and retires everyone's reads of stage c-1.
-      int after = LS * (min(nch - 1, c + 2) - c);
-      for (int i = max(0, c - 3); i < c; ++i) after += (i % WS == 0 && i / WS + 1 < nwin) ? 1 : 0;
-      wait_vmcnt(after);
-      __syncthreads();
-      if (c + kRingStages - 1 < nch)
-        ring_issue<BM, WAVES>(ring0 + ((c + kRingStages - 1) % kRingStages) * L::kStage, rw, rx,
-                              off, K, u.k_beg + (c + kRingStages - 1) * kRingKC, u.k_end, wave);
-      // window c/4 + 1 reuses the slot of window c/4 - 1, which every wave
-      // finished before this barrier; it is first read four iterations later
-      if (c % WS == 0 && c / WS + 1 < nwin)
-        ring_issue_scales(ring0 + L::kSWin + ((c / WS + 1) & 1) * L::kWinBytes, rs, off.s,
-                          u.k_beg + (c / WS + 1) * WS * kRingKC, wave);
-      StageRegs<BM, WAVES> r;
-      ring_read<BM, WAVES>(r, ring + (c % kRingStages) * L::kStage,
-                           ring + L::kSWin + ((c / WS) & 1) * L::kWinBytes, c % WS,
-                           u.k_beg + c * kRingKC + 32 * q < u.k_end, wave, lane);
-      ring_mma<BM, WAVES>(acc, r);
+#define NVFP4_KLOOP(NFE) \
+  kp_kloop<BM, NSLOT, KW, BN, NFE>(acc, ring, u, rw, rs, rx, off, kp, ch, wave, lane)
+    switch (nf) {
+      case 1: NVFP4_KLOOP(1); break;
+      case 2: NVFP4_KLOOP(NF >= 2 ? 2 : NF); break;
+      case 3: NVFP4_KLOOP(NF >= 3 ? 3 : NF); break;
+      default: NVFP4_KLOOP(NF); break;
     }
-    __syncthreads();  // every wave is done with the ring before the next unit refills it
-    finish_tile<NF, NW, WAVES>(acc, p, u, sc);
+#undef NVFP4_KLOOP
+
+    // Sum the two K halves: wave w keeps column tiles [NH kp, NH kp + NH) of
+    // its NJ and hands the others to wave w ^ 1 through LDS (the ring is idle).
+    __syncthreads();
+    f32x4_t* red = reinterpret_cast<f32x4_t*>(ring) + wave * (NF * NH * kWave) + lane;
+    const f32x4_t* peer =
+        reinterpret_cast<const f32x4_t*>(ring) + (wave ^ 1) * (NF * NH * kWave) + lane;
+    f32x4_t out[NF][NH];
+    // (the branch is wave-uniform; both sides index the accumulators with
+    // constants so they stay in registers)
+    if (kp == 0) {
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int jj = 0; jj < NH; ++jj) red[(f * NH + jj) * kWave] = acc[f][NH + jj];
+      __syncthreads();
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int jj = 0; jj < NH; ++jj) out[f][jj] = acc[f][jj] + peer[(f * NH + jj) * kWave];
+    } else {
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int jj = 0; jj < NH; ++jj) red[(f * NH + jj) * kWave] = acc[f][jj];
+      __syncthreads();
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int jj = 0; jj < NH; ++jj) out[f][jj] = peer[(f * NH + jj) * kWave] + acc[f][NH + jj];
+    }
+    __syncthreads();  // the ring is free for the next unit's loads
+    // wave w now owns columns [w CPW/2, (w + 1) CPW/2) of the unit
+    finish_tile<NF, NH, KW, BN>(out, p, u, sc);
   }
 }
 
@@ -524,6 +599,7 @@ constexpr int kRegThreads = 256;   // 4 waves
 constexpr int kRegWaves = kRegThreads / kWave;
 constexpr int kNW = 4;             // MFMA column tiles per wave
 constexpr int kKC = 256;           // K per chunk
+constexpr int kRegBN = kRegWaves * kNW * 16;  // columns per unit (256)
 constexpr int kLdsStride = kKC + 8;  // BF16 elements per staged activation row (16 B pad)
 
 // One lane's packed weights (8 dwords = 64 nibbles along K) and its 4 block
@@ -633,7 +709,7 @@ __global__ __launch_bounds__(kRegThreads) void gemm_reg_kernel(GemmParams p) {
         make_rsrc(p.s + (int64_t)u.e * N * (K / 16), (uint32_t)N * (uint32_t)(K / 16));
     int nrow[kNW];
 #pragma unroll
-    for (int j = 0; j < kNW; ++j) nrow[j] = u.nt * kBN + wave * (kNW * 16) + j * 16 + r16;
+    for (int j = 0; j < kNW; ++j) nrow[j] = u.nt * kRegBN + wave * (kNW * 16) + j * 16 + r16;
 
     f32x4_t acc[NF][kNW];
 #pragma unroll
@@ -670,7 +746,7 @@ __global__ __launch_bounds__(kRegThreads) void gemm_reg_kernel(GemmParams p) {
       if (more2) store_xtile<BM>(xs[0], xr, tid);
       __syncthreads();
     }
-    finish_tile<NF, kNW, kRegWaves>(acc, p, u, sc);
+    finish_tile<NF, kNW, kRegWaves, kRegBN>(acc, p, u, sc);
   }
 }
 
@@ -706,34 +782,42 @@ static int env_int(const char* name, int dflt) {
   return atoi(v);
 }
 
-static int ring_waves() {
-  const int w = env_int("NVFP4_RING_WAVES", 8);
-  return w == 16 ? 16 : 8;
+// Kernel configuration of a plan (GemmPlan::kind):
+//   0  register kernel, 4 waves x 256 columns (any k % 16 == 0)
+//   1  K-phase kernel, 4 waves x 128 columns, two workgroups per CU (tiles of
+//      up to 32 rows)
+//   2  K-phase kernel, 8 waves x 256 columns (64-row tiles, or any tile size
+//      with NVFP4_KPCFG=8)
+static void choose_kernel(GemmPlan& pl) {
+  if (!pl.fast) {
+    pl.kind = 0; pl.bn = 256; pl.nslot = 0;
+  } else if (pl.bm <= 32 && env_int("NVFP4_KPCFG", 4) != 8) {
+    pl.kind = 1; pl.bn = 128; pl.nslot = pl.bm == 16 ? 5 : 4;
+  } else {
+    pl.kind = 2; pl.bn = 256; pl.nslot = pl.bm == 64 ? 4 : 5;
+  }
 }
 
-static int occupancy_for(int bm, bool ring) {
+static int occupancy_for(const GemmPlan& pl) {
   static int cache[3][3] = {{-1, -1, -1}, {-1, -1, -1}, {-1, -1, -1}};
-  const int bi = bm == 16 ? 0 : (bm == 32 ? 1 : 2);
-  const int rw = ring_waves();
-  int& c = cache[ring ? (rw == 16 ? 2 : 1) : 0][bi];
+  const int bi = pl.bm == 16 ? 0 : (pl.bm == 32 ? 1 : 2);
+  int& c = cache[pl.kind][bi];
   if (c < 0) {
-    if (ring && rw == 16) {
-      c = bm == 16 ? occupancy_of(gemm_ring_kernel<16, 16>, 1024)
-                   : bm == 32 ? occupancy_of(gemm_ring_kernel<32, 16>, 1024)
-                              : occupancy_of(gemm_ring_kernel<64, 16>, 1024);
-    } else if (ring) {
-      c = bm == 16 ? occupancy_of(gemm_ring_kernel<16, 8>, 512)
-                   : bm == 32 ? occupancy_of(gemm_ring_kernel<32, 8>, 512)
-                              : occupancy_of(gemm_ring_kernel<64, 8>, 512);
+    if (pl.kind == 0) {
+      c = pl.bm == 16 ? occupancy_of(gemm_reg_kernel<16>, kRegThreads)
+          : pl.bm == 32 ? occupancy_of(gemm_reg_kernel<32>, kRegThreads)
+                        : occupancy_of(gemm_reg_kernel<64>, kRegThreads);
+    } else if (pl.kind == 1) {
+      c = pl.bm == 16 ? occupancy_of(gemm_kp_kernel<16, 5, 4, 128>, 256)
+                      : occupancy_of(gemm_kp_kernel<32, 4, 4, 128>, 256);
     } else {
-      c = bm == 16 ? occupancy_of(gemm_reg_kernel<16>, kRegThreads)
-                   : bm == 32 ? occupancy_of(gemm_reg_kernel<32>, kRegThreads)
-                              : occupancy_of(gemm_reg_kernel<64>, kRegThreads);
+      c = pl.bm == 16 ? occupancy_of(gemm_kp_kernel<16, 5, 8, 256>, 512)
+          : pl.bm == 32 ? occupancy_of(gemm_kp_kernel<32, 5, 8, 256>, 512)
+                        : occupancy_of(gemm_kp_kernel<64, 4, 8, 256>, 512);
     }
   }
   return c;
 }
-
 
 GemmPlan plan_gemm(int64_t rows, int64_t num_experts, int64_t n, int64_t k, bool grouped,
                    int cu_count) {
@@ -746,13 +830,14 @@ GemmPlan plan_gemm(int64_t rows, int64_t num_experts, int64_t n, int64_t k, bool
   const int force_bm = env_int("NVFP4_BM", 0);
   if (force_bm == 16 || force_bm == 32 || force_bm == 64) bm = force_bm;
   pl.bm = bm;
-  pl.n_tiles = (int)((n + kBN - 1) / kBN);
+  choose_kernel(pl);
+  pl.n_tiles = (int)((n + pl.bn - 1) / pl.bn);
   // Upper bound on output tiles: each non-empty expert adds at most one
   // partial row tile beyond rows / bm.
   const int64_t mt_bound = grouped ? (rows + bm - 1) / bm + std::min<int64_t>(num_experts, rows)
                                    : (rows + bm - 1) / bm;
   const int64_t max_tiles = mt_bound * pl.n_tiles;
-  const int64_t occ = occupancy_for(bm, pl.fast);
+  const int64_t occ = occupancy_for(pl);
   const int64_t slots = (int64_t)cu_count * occ;
   // Split K only when there are too few tiles to occupy the resident slots.
   const int align = pl.fast ? 64 : 16;
@@ -776,29 +861,30 @@ GemmPlan plan_gemm(int64_t rows, int64_t num_experts, int64_t n, int64_t k, bool
   pl.max_tiles = (int)max_tiles;
   const int64_t units_bound = max_tiles * splits;
   pl.grid = (int)std::max<int64_t>(1, std::min<int64_t>(slots, units_bound));
-  pl.ws_bytes = splits > 1 ? kCounterBytes + (size_t)max_tiles * splits * bm * kBN * sizeof(float)
-                           : 0;
+  pl.ws_bytes = splits > 1
+                    ? kCounterBytes + (size_t)max_tiles * splits * bm * pl.bn * sizeof(float)
+                    : 0;
   return pl;
 }
 
 hipError_t launch_gemm(const GemmPlan& pl, const GemmParams& p, hipStream_t stream) {
   dim3 grid(pl.grid);
-  if (pl.fast && ring_waves() == 16) {
-    dim3 block(1024);
-    if (pl.bm == 16) hipLaunchKernelGGL((gemm_ring_kernel<16, 16>), grid, block, 0, stream, p);
-    else if (pl.bm == 32) hipLaunchKernelGGL((gemm_ring_kernel<32, 16>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((gemm_ring_kernel<64, 16>), grid, block, 0, stream, p);
-  } else if (pl.fast) {
-    dim3 block(512);
-    if (pl.bm == 16) hipLaunchKernelGGL((gemm_ring_kernel<16, 8>), grid, block, 0, stream, p);
-    else if (pl.bm == 32) hipLaunchKernelGGL((gemm_ring_kernel<32, 8>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((gemm_ring_kernel<64, 8>), grid, block, 0, stream, p);
+#define NVFP4_KP(BM, NS, KW, BN) \
+  hipLaunchKernelGGL((gemm_kp_kernel<BM, NS, KW, BN>), grid, dim3(KW * 64), 0, stream, p)
+  if (pl.kind == 1) {
+    if (pl.bm == 16) NVFP4_KP(16, 5, 4, 128);
+    else NVFP4_KP(32, 4, 4, 128);
+  } else if (pl.kind == 2) {
+    if (pl.bm == 16) NVFP4_KP(16, 5, 8, 256);
+    else if (pl.bm == 32) NVFP4_KP(32, 5, 8, 256);
+    else NVFP4_KP(64, 4, 8, 256);
   } else {
     dim3 block(kRegThreads);
     if (pl.bm == 16) hipLaunchKernelGGL(gemm_reg_kernel<16>, grid, block, 0, stream, p);
     else if (pl.bm == 32) hipLaunchKernelGGL(gemm_reg_kernel<32>, grid, block, 0, stream, p);
     else hipLaunchKernelGGL(gemm_reg_kernel<64>, grid, block, 0, stream, p);
   }
+#undef NVFP4_KP
   return hipGetLastError();
 }
 

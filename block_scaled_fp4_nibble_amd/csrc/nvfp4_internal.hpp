@@ -20,9 +20,6 @@ hipError_t launch_quantize(const uint16_t* w, int64_t batch, int64_t n, int64_t 
                            uint32_t* partial, int parts, hipStream_t stream);
 
 // ---- GEMM ---------------------------------------------------------------
-// Output columns (weight rows) covered by one work unit.
-constexpr int kBN = 256;
-
 struct GemmParams {
   const uint16_t* x;        // [rows][k] bf16
   const uint8_t* w;         // [E][n][k/2]
@@ -39,13 +36,16 @@ struct GemmParams {
   int32_t k;
   int32_t splits;           // K splits per output tile
   int32_t k_split;          // K per split (multiple of 64 on the fast path, of 16 otherwise)
-  int32_t n_tiles;          // ceil(n / kBN)
+  int32_t n_tiles;          // ceil(n / column tile width of the chosen kernel)
   int32_t total_units;      // exact for dense, -1 for grouped (computed on device)
   int32_t out_f32;
 };
 
 struct GemmPlan {
   int bm;        // rows per tile: 16, 32 or 64
+  int kind;      // kernel configuration (see plan_gemm)
+  int bn;        // columns per tile: 128 or 256
+  int nslot;     // LDS ring slots of the K-phase kernel
   int splits;
   int k_split;
   int n_tiles;

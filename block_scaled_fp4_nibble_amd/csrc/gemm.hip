@@ -135,10 +135,17 @@ __device__ int build_schedule(Sched& sc, const GemmParams& p) {
   const int E = p.num_experts;
   constexpr int PER = (kMaxExperts + THREADS - 1) / THREADS;  // experts per thread
   int bad = 0, my_units = 0;
-  for (int e = PER * tid; e < PER * tid + PER && e < E; ++e) {
-    const int a = seg_begin(p, e), b = seg_begin(p, e + 1);
-    bad |= b < a;
-    my_units += (b - a + BM - 1) / BM * p.n_tiles * p.splits;
+  int cnt[PER];
+#pragma unroll
+  for (int t = 0; t < PER; ++t) {
+    const int e = PER * tid + t;
+    cnt[t] = 0;
+    if (e < E) {
+      const int a = seg_begin(p, e), b = seg_begin(p, e + 1);
+      bad |= b < a;
+      cnt[t] = (b - a + BM - 1) / BM * p.n_tiles * p.splits;
+      my_units += cnt[t];
+    }
   }
   if (tid == 0) bad |= (seg_begin(p, 0) != 0) | ((int64_t)seg_begin(p, E) != p.rows);
   bad = __syncthreads_or(bad);
@@ -149,9 +156,11 @@ __device__ int build_schedule(Sched& sc, const GemmParams& p) {
   }
   int total_units;
   int ubase = block_exclusive_scan<THREADS>(my_units, sc.tmp, &total_units);
-  for (int e = PER * tid; e < PER * tid + PER && e < E; ++e) {
-    sc.units[e] = ubase;
-    ubase += (seg_begin(p, e + 1) - seg_begin(p, e) + BM - 1) / BM * p.n_tiles * p.splits;
+#pragma unroll
+  for (int t = 0; t < PER; ++t) {
+    const int e = PER * tid + t;
+    if (e < E) sc.units[e] = ubase;
+    ubase += cnt[t];
   }
   if (tid == 0) sc.units[E] = total_units;
   __syncthreads();
@@ -208,7 +217,7 @@ __device__ __forceinline__ Unit decode_unit(const Sched& sc, const GemmParams& p
 // Returns false when another split of the tile will finish it.
 template <int NF, int NW, int WAVES, int BN>
 __device__ __forceinline__ bool finish_tile(f32x4_t (&acc)[NF][NW], const GemmParams& p,
-                                            const Unit& u, Sched& sc) {
+                                            const Unit& u, float gv, Sched& sc) {
   constexpr int BM = NF * 16;
   static_assert(WAVES * NW * 16 == BN, "waves cover the column tile");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -246,7 +255,6 @@ __device__ __forceinline__ bool finish_tile(f32x4_t (&acc)[NF][NW], const GemmPa
       }
     if (tid == 0) p.counters[u.tile] = 0u;
   }
-  const float gv = p.g[u.e];
   const int q = lane >> 4, r16 = lane & 15;
 #pragma unroll
   for (int f = 0; f < NF; ++f)
@@ -273,18 +281,24 @@ __device__ __forceinline__ bool finish_tile(f32x4_t (&acc)[NF][NW], const GemmPa
 
 constexpr int kRingKC = 128;       // K per stage
 
-// s_waitcnt vmcnt(n) for a run-time n in [0, 15]: the immediate must be a
-// constant.  Encoding (gfx9): vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits
-// 15:14, expcnt and lgkmcnt left at their maxima (no wait on them).
+// s_waitcnt vmcnt(n) for a run-time n: the immediate must be a constant.
+// Encoding (gfx9): vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt
+// and lgkmcnt left at their maxima (no wait on them).  n >= 63 needs no
+// wait (the counter cannot exceed 63); n <= 0 waits for everything.
 __device__ __forceinline__ void wait_vmcnt(int n) {
 #define NVFP4_VMCNT(v) \
   case v: __builtin_amdgcn_s_waitcnt(((v) & 15) | (((v) >> 4) << 14) | (7 << 4) | (15 << 8)); break;
+#define NVFP4_VMCNT8(b) NVFP4_VMCNT(b) NVFP4_VMCNT(b + 1) NVFP4_VMCNT(b + 2) NVFP4_VMCNT(b + 3) \
+  NVFP4_VMCNT(b + 4) NVFP4_VMCNT(b + 5) NVFP4_VMCNT(b + 6) NVFP4_VMCNT(b + 7)
+  if (n >= 63) return;
   switch (n) {
-    NVFP4_VMCNT(1) NVFP4_VMCNT(2) NVFP4_VMCNT(3) NVFP4_VMCNT(4) NVFP4_VMCNT(5) NVFP4_VMCNT(6)
-    NVFP4_VMCNT(7) NVFP4_VMCNT(8) NVFP4_VMCNT(9) NVFP4_VMCNT(10) NVFP4_VMCNT(11)
-    NVFP4_VMCNT(12) NVFP4_VMCNT(13) NVFP4_VMCNT(14) NVFP4_VMCNT(15)
+    NVFP4_VMCNT8(8) NVFP4_VMCNT8(16) NVFP4_VMCNT8(24) NVFP4_VMCNT8(32) NVFP4_VMCNT8(40)
+    NVFP4_VMCNT8(48) NVFP4_VMCNT(1) NVFP4_VMCNT(2) NVFP4_VMCNT(3) NVFP4_VMCNT(4)
+    NVFP4_VMCNT(5) NVFP4_VMCNT(6) NVFP4_VMCNT(7) NVFP4_VMCNT(56) NVFP4_VMCNT(57)
+    NVFP4_VMCNT(58) NVFP4_VMCNT(59) NVFP4_VMCNT(60) NVFP4_VMCNT(61) NVFP4_VMCNT(62)
     default: __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8)); break;
   }
+#undef NVFP4_VMCNT8
 #undef NVFP4_VMCNT
 }
 
@@ -436,20 +450,27 @@ __device__ __forceinline__ void kp_read(KpRegs<BM, NJ>& r, const uint8_t* stage,
                                                      16 * ((8 * kp + 2 * q + i) ^ r16));
 }
 
+// Multiply out one stage held in registers.  The B fragment of step t + 1
+// is dequantized while the MFMAs of step t run.
 template <int BM, int NJ, int NFE>
 __device__ __forceinline__ void kp_mma(f32x4_t (&acc)[BM / 16][NJ], const KpRegs<BM, NJ>& r) {
   float scl[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) scl[j] = decode_e4m3<0>(r.sc[j]);
+  constexpr int T = 2 * NJ;
+  bf16x8_t b[2];
+  b[0] = dequant8(r.wd[0][0], scl[0]);
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const bf16x8_t b = dequant8(r.wd[j][i], scl[j]);
-#pragma unroll
-      for (int f = 0; f < NFE; ++f)
-        acc[f][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.a[i][f], b, acc[f][j], 0, 0, 0);
+  for (int t = 0; t < T; ++t) {
+    const int i = t / NJ, j = t % NJ;
+    if (t + 1 < T) {
+      const int i1 = (t + 1) / NJ, j1 = (t + 1) % NJ;
+      b[(t + 1) & 1] = dequant8(r.wd[j1][i1], scl[j1]);
     }
+#pragma unroll
+    for (int f = 0; f < NFE; ++f)
+      acc[f][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.a[i][f], b[t & 1], acc[f][j], 0, 0, 0);
+  }
 }
 
 // The K loop of one unit, for tiles whose rows fill NFE of the BM / 16 row
@@ -538,6 +559,7 @@ __global__ __launch_bounds__(KW * 64) void gemm_kp_kernel(GemmParams p) {
     const u32x4_t rx =
         rsrc_words(p.x + (int64_t)u.row0 * K, (uint32_t)(u.row_end - u.row0) * (uint32_t)(K * 2));
     const KpOffsets<BM, KW, BN> off = kp_offsets<BM, KW, BN>(n0, K, wave, lane);
+    const float gv = p.g[u.e];  // issued now, first used in the epilogue
     // 16-row fragments holding rows of this tile (the rest is padding)
     const int nf = min(NF, (u.row_end - u.row0 + 15) / 16);
 
@@ -589,7 +611,7 @@ __global__ __launch_bounds__(KW * 64) void gemm_kp_kernel(GemmParams p) {
     }
     __syncthreads();  // the ring is free for the next unit's loads
     // wave w now owns columns [w CPW/2, (w + 1) CPW/2) of the unit
-    finish_tile<NF, NH, KW, BN>(out, p, u, sc);
+    finish_tile<NF, NH, KW, BN>(out, p, u, gv, sc);
   }
 }
 
@@ -746,7 +768,7 @@ __global__ __launch_bounds__(kRegThreads) void gemm_reg_kernel(GemmParams p) {
       if (more2) store_xtile<BM>(xs[0], xr, tid);
       __syncthreads();
     }
-    finish_tile<NF, kNW, kRegWaves, kRegBN>(acc, p, u, sc);
+    finish_tile<NF, kNW, kRegWaves, kRegBN>(acc, p, u, p.g[u.e], sc);
   }
 }
 

@@ -147,7 +147,7 @@ __device__ int build_schedule(Sched& sc, const GemmParams& p) {
       my_units += cnt[t];
     }
   }
-  if (tid == 0) bad |= (seg_begin(p, 0) != 0) | ((int64_t)seg_begin(p, E) != p.rows);
+  if (tid == 0) bad |= (seg_begin(p, 0) != 0) || ((int64_t)seg_begin(p, E) != p.rows);
   bad = __syncthreads_or(bad);
   if (bad) {
     if (blockIdx.x == 0 && tid == 0 && p.d_status != nullptr)
@@ -615,6 +615,258 @@ __global__ __launch_bounds__(KW * 64) void gemm_kp_kernel(GemmParams p) {
   }
 }
 
+// ---- large-M kernel (k % 64 == 0, many rows) -----------------------------------
+//
+// For a dense product with at least a few hundred rows the weight tile is
+// worth dequantizing once into LDS and sharing across a large row tile: a
+// 256 x 256 output tile per workgroup of 4 waves (one per SIMD), each wave
+// a 128 x 128 quadrant of 4 x 4 v_mfma_f32_32x32x16_bf16 tiles (FP32
+// accumulators in AGPRs).  K advances in 64-wide steps through a 3-stage LDS
+// ring holding, per step, the activation tile (256 rows x 128 B) and the
+// packed weight tile (256 rows x 32 B); block scales arrive in windows of 4
+// steps (256 rows x 16 B).  Per step each wave reads its A and B fragments
+// from LDS, runs 64 MFMAs, and after a barrier dequantizes 64 weight rows of
+// the next step into the shared BF16 weight tile (256 rows x 128 B).
+//
+// LDS rows of the activation and BF16 weight tiles keep their 16-byte
+// chunk c in slot c ^ ((r >> 1) & 7), so the 32-row fragment reads and the
+// dequantizer's row writes spread over all banks.
+constexpr int kLmBM = 256, kLmBN = 256, kLmBK = 64;
+
+struct LmLayout {
+  static constexpr int kXStage = kLmBM * kLmBK * 2;          // 32 KB
+  static constexpr int kWpStage = kLmBN * kLmBK / 2;         // 8 KB
+  static constexpr int kStage = kXStage + kWpStage;
+  static constexpr int kStages = 3;
+  static constexpr int kWbf = kStages * kStage;              // BF16 weight tile, 32 KB
+  static constexpr int kWin = kWbf + kLmBN * kLmBK * 2;      // 2 scale windows of 4 KB
+  static constexpr int kWinBytes = kLmBN * 16;
+  static constexpr int kTotal = kWin + 2 * kWinBytes;
+  static constexpr int kXLoads = kXStage / 1024 / 4;         // per wave per step: 8
+  static constexpr int kWpLoads = kWpStage / 1024 / 4;       // per wave per step: 2
+  static constexpr int kLoadsPerStage = kXLoads + kWpLoads;
+  static_assert(kTotal <= 160 * 1024, "LDS budget");
+};
+
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+
+__device__ __forceinline__ int lm_swz(int r, int c) { return r * 128 + 16 * (c ^ ((r >> 1) & 7)); }
+
+struct LmOffsets {
+  uint32_t x[LmLayout::kXLoads];
+  uint32_t wp[LmLayout::kWpLoads];
+  uint32_t s;
+};
+
+__device__ __forceinline__ LmOffsets lm_offsets(int K, int wave, int lane) {
+  LmOffsets o;
+  // activations: load t covers tile rows 8t..8t+7 (128 B each); slot c of
+  // row r receives chunk c ^ ((r >> 1) & 7)
+#pragma unroll
+  for (int tt = 0; tt < LmLayout::kXLoads; ++tt) {
+    const int r = (wave * LmLayout::kXLoads + tt) * 8 + (lane >> 3);
+    const int g = (lane & 7) ^ ((r >> 1) & 7);
+    o.x[tt] = (uint32_t)r * (uint32_t)(K * 2) + (uint32_t)(16 * g);
+  }
+  // packed weights: load t covers rows 32t..32t+31 (32 B each, unswizzled)
+#pragma unroll
+  for (int tt = 0; tt < LmLayout::kWpLoads; ++tt) {
+    const int r = (wave * LmLayout::kWpLoads + tt) * 32 + (lane >> 1);
+    o.wp[tt] = (uint32_t)r * (uint32_t)(K / 2) + (uint32_t)(16 * (lane & 1));
+  }
+  // scale window: wave w loads rows 64w..64w+63, 16 B (256 K) each
+  o.s = (uint32_t)(wave * 64 + lane) * (uint32_t)(K / 16);
+  return o;
+}
+
+__device__ __forceinline__ void lm_issue(uint32_t ring0, int step, u32x4_t rx, u32x4_t rw,
+                                         u32x4_t rs, const LmOffsets& o, int wave) {
+  // order: scale window (with the first step it covers), packed weights,
+  // activations -- the weights of a step are needed one step earlier
+  if (step % 4 == 0)
+    lds_dma16(ring0 + LmLayout::kWin + ((step / 4) & 1) * LmLayout::kWinBytes + wave * 1024, o.s,
+              (uint32_t)(step * kLmBK / 16), rs);
+  const uint32_t st = ring0 + (step % LmLayout::kStages) * LmLayout::kStage;
+#pragma unroll
+  for (int tt = 0; tt < LmLayout::kWpLoads; ++tt)
+    lds_dma16(st + LmLayout::kXStage + (wave * LmLayout::kWpLoads + tt) * 1024, o.wp[tt],
+              (uint32_t)(step * kLmBK / 2), rw);
+#pragma unroll
+  for (int tt = 0; tt < LmLayout::kXLoads; ++tt)
+    lds_dma16(st + (wave * LmLayout::kXLoads + tt) * 1024, o.x[tt], (uint32_t)(step * kLmBK * 2),
+              rx);
+}
+
+// One lane's share of a weight step: row 64 wave + lane, 64 K = 8 dwords of
+// nibbles and the row's 4 block scales of the step.
+struct LmWp {
+  uint32_t d[8];
+  float sv[4];
+};
+
+__device__ __forceinline__ void lm_read_wp(LmWp& w, const uint8_t* ring, int step, int wave, int lane) {
+  const int r = wave * 64 + lane;
+  const uint8_t* wp = ring + (step % LmLayout::kStages) * LmLayout::kStage + LmLayout::kXStage + r * 32;
+  const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(wp);
+  const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(wp + 16);
+  const uint32_t sc = *reinterpret_cast<const uint32_t*>(
+      ring + LmLayout::kWin + ((step / 4) & 1) * LmLayout::kWinBytes + r * 16 + 4 * (step % 4));
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    w.d[c] = lo[c];
+    w.d[4 + c] = hi[c];
+  }
+  w.sv[0] = decode_e4m3<0>(sc);
+  w.sv[1] = decode_e4m3<1>(sc);
+  w.sv[2] = decode_e4m3<2>(sc);
+  w.sv[3] = decode_e4m3<3>(sc);
+}
+
+// Write a dequantized row (8 chunks of 8 BF16) into the BF16 weight tile.
+__device__ __forceinline__ void lm_write_wbf(uint8_t* ring, const bf16x8_t (&v)[8], int wave, int lane) {
+  const int r = wave * 64 + lane;
+  uint8_t* wb = ring + LmLayout::kWbf;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) *reinterpret_cast<bf16x8_t*>(wb + lm_swz(r, c)) = v[c];
+}
+
+// 64 MFMAs of one step for the wave's 128 x 128 quadrant: 4 K sub-steps of
+// 16, each reading 4 A and 4 B fragments (lane l: row / column l % 32,
+// K 8 (l / 32) .. +7 of the sub-step).  The next step's weight row is
+// dequantized into registers between the MFMAs (chunk 2 ks + half after
+// each group of 8), where its VALU work overlaps the matrix pipeline.
+__device__ __forceinline__ void lm_frags(bf16x8_t (&a)[4], bf16x8_t (&b)[4], const uint8_t* xs,
+                                         const uint8_t* wb, int ks, int wm, int wn, int lane) {
+  const int r32 = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    a[i] = *reinterpret_cast<const bf16x8_t*>(xs + lm_swz(wm * 128 + i * 32 + r32, 2 * ks + h));
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    b[j] = *reinterpret_cast<const bf16x8_t*>(wb + lm_swz(wn * 128 + j * 32 + r32, 2 * ks + h));
+}
+
+__device__ __forceinline__ void lm_mma(f32x16_t (&acc)[4][4], const uint8_t* xs, const uint8_t* wb,
+                                       int wm, int wn, int lane, bool dq, const LmWp& w,
+                                       bf16x8_t (&v)[8]) {
+  // fragments of sub-step ks + 1 are read while sub-step ks is multiplied
+  bf16x8_t a[2][4], b[2][4];
+  lm_frags(a[0], b[0], xs, wb, 0, wm, wn, lane);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    if (ks + 1 < 4) lm_frags(a[(ks + 1) & 1], b[(ks + 1) & 1], xs, wb, ks + 1, wm, wn, lane);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int i = 2 * half; i < 2 * half + 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks & 1][i], b[ks & 1][j], acc[i][j],
+                                                              0, 0, 0);
+      if (dq) {
+        const int c = 2 * ks + half;
+        v[c] = dequant8(w.d[c], w.sv[c >> 1]);
+      }
+    }
+  }
+}
+
+// Dense only (offsets == nullptr, one expert): tile t of the grid is
+// (row tile t / n_tiles, column tile t % n_tiles) after an XCD-aware remap.
+__global__ __launch_bounds__(256) void gemm_lm_kernel(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring[LmLayout::kTotal];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int N = p.n, K = p.k;
+  const int m_tiles = (int)((p.rows + kLmBM - 1) / kLmBM);
+  const int total = m_tiles * p.n_tiles;
+  const uint32_t ring0 = lds_addr(ring);
+  const LmOffsets off = lm_offsets(K, wave, lane);
+  const int nsteps = K / kLmBK;
+  constexpr int LS = LmLayout::kLoadsPerStage;
+  const float gv = p.g[0];
+
+  for (int round = 0; round * (int)gridDim.x < total; ++round) {
+    const int t = round_unit(round, blockIdx.x, gridDim.x);
+    if (t >= total) continue;
+    const int mt = t / p.n_tiles, nt = t % p.n_tiles;
+    const int row0 = mt * kLmBM, n0 = nt * kLmBN;
+    const int row_end = (int)min((int64_t)row0 + kLmBM, p.rows);
+    const u32x4_t rx = rsrc_words(p.x + (int64_t)row0 * K, (uint32_t)(row_end - row0) * (uint32_t)(K * 2));
+    const u32x4_t rw = rsrc_words(p.w + (int64_t)n0 * (K / 2),
+                                  (uint32_t)(min(N - n0, kLmBN)) * (uint32_t)(K / 2));
+    const u32x4_t rs = rsrc_words(p.s + (int64_t)n0 * (K / 16),
+                                  (uint32_t)(min(N - n0, kLmBN)) * (uint32_t)(K / 16));
+
+    f32x16_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+    // Pipeline per iteration s (in issue order): wait until step s + 1's
+    // packed weights have landed (only its activations may still be in
+    // flight), barrier, issue step s + 2 into the slot step s - 1 used, then
+    // run step s's MFMAs from LDS with step s + 1's weights dequantized into
+    // registers between them; after a second barrier (every wave has read
+    // the BF16 tile of step s) those registers become the BF16 tile of
+    // step s + 1.
+    LmWp wq;
+    bf16x8_t v[8];
+    lm_issue(ring0, 0, rx, rw, rs, off, wave);
+    if (nsteps > 1) lm_issue(ring0, 1, rx, rw, rs, off, wave);
+    // step 0 complete: only step 1's loads may remain
+    wait_vmcnt(nsteps > 1 ? LS : 0);
+    __syncthreads();
+    lm_read_wp(wq, ring, 0, wave, lane);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) v[c] = dequant8(wq.d[c], wq.sv[c >> 1]);
+    lm_write_wbf(ring, v, wave, lane);
+
+    for (int s = 0; s < nsteps; ++s) {
+      const bool more = s + 1 < nsteps;
+      // the packed weights of step s + 1 precede its activations in issue
+      // order; the activations (LX loads) may still be in flight
+      wait_vmcnt(more ? LmLayout::kXLoads : 0);
+      __syncthreads();
+      if (s + 2 < nsteps) lm_issue(ring0, s + 2, rx, rw, rs, off, wave);
+      if (more) lm_read_wp(wq, ring, s + 1, wave, lane);
+      lm_mma(acc, ring + (s % LmLayout::kStages) * LmLayout::kStage, ring + LmLayout::kWbf, wm, wn,
+             lane, more, wq, v);
+      if (more) {
+        __syncthreads();
+        lm_write_wbf(ring, v, wave, lane);
+      }
+    }
+    __syncthreads();  // all fragment reads done before the next tile's loads
+
+    // epilogue: lane l of tile (i, j) holds column l % 32 and rows
+    // 8 (e / 4) + 4 (l / 32) + e % 4 of the 32 x 32 block
+    const int r32 = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int col = n0 + wn * 128 + j * 32 + r32;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = row0 + wm * 128 + i * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+          if (row < row_end && col < N) {
+            const float v = gv * acc[i][j][e];
+            if (p.out_f32)
+              reinterpret_cast<float*>(p.y)[(int64_t)row * N + col] = v;
+            else
+              reinterpret_cast<uint16_t*>(p.y)[(int64_t)row * N + col] =
+                  (uint16_t)float_to_bf16_rne(v);
+          }
+        }
+      }
+  }
+}
+
 // ---- register kernel (any k % 16 == 0) ------------------------------------------
 
 constexpr int kRegThreads = 256;   // 4 waves
@@ -810,8 +1062,14 @@ static int env_int(const char* name, int dflt) {
 //      up to 32 rows)
 //   2  K-phase kernel, 8 waves x 256 columns (64-row tiles, or any tile size
 //      with NVFP4_KPCFG=8)
-static void choose_kernel(GemmPlan& pl) {
-  if (!pl.fast) {
+//   3  large-M kernel, 256 x 256 tiles (dense products with at least
+//      kLmMinRows rows; NVFP4_LM=0 disables it)
+constexpr int kLmMinRows = 256;
+
+static void choose_kernel(GemmPlan& pl, int64_t rows, bool grouped) {
+  if (pl.fast && !grouped && rows >= kLmMinRows && env_int("NVFP4_LM", 1) != 0) {
+    pl.kind = 3; pl.bn = kLmBN; pl.bm = kLmBM;
+  } else if (!pl.fast) {
     pl.kind = 0; pl.bn = 256; pl.nslot = 0;
   } else if (pl.bm <= 32 && env_int("NVFP4_KPCFG", 4) != 8) {
     pl.kind = 1; pl.bn = 128; pl.nslot = pl.bm == 16 ? 5 : 4;
@@ -821,7 +1079,7 @@ static void choose_kernel(GemmPlan& pl) {
 }
 
 static int occupancy_for(const GemmPlan& pl) {
-  static int cache[3][3] = {{-1, -1, -1}, {-1, -1, -1}, {-1, -1, -1}};
+  static int cache[4][3] = {{-1, -1, -1}, {-1, -1, -1}, {-1, -1, -1}, {-1, -1, -1}};
   const int bi = pl.bm == 16 ? 0 : (pl.bm == 32 ? 1 : 2);
   int& c = cache[pl.kind][bi];
   if (c < 0) {
@@ -829,6 +1087,8 @@ static int occupancy_for(const GemmPlan& pl) {
       c = pl.bm == 16 ? occupancy_of(gemm_reg_kernel<16>, kRegThreads)
           : pl.bm == 32 ? occupancy_of(gemm_reg_kernel<32>, kRegThreads)
                         : occupancy_of(gemm_reg_kernel<64>, kRegThreads);
+    } else if (pl.kind == 3) {
+      c = occupancy_of(gemm_lm_kernel, 256);
     } else if (pl.kind == 1) {
       c = pl.bm == 16 ? occupancy_of(gemm_kp_kernel<16, 5, 4, 128>, 256)
                       : occupancy_of(gemm_kp_kernel<32, 4, 4, 128>, 256);
@@ -852,7 +1112,8 @@ GemmPlan plan_gemm(int64_t rows, int64_t num_experts, int64_t n, int64_t k, bool
   const int force_bm = env_int("NVFP4_BM", 0);
   if (force_bm == 16 || force_bm == 32 || force_bm == 64) bm = force_bm;
   pl.bm = bm;
-  choose_kernel(pl);
+  choose_kernel(pl, rows, grouped);
+  bm = pl.bm;
   pl.n_tiles = (int)((n + pl.bn - 1) / pl.bn);
   // Upper bound on output tiles: each non-empty expert adds at most one
   // partial row tile beyond rows / bm.
@@ -893,7 +1154,9 @@ hipError_t launch_gemm(const GemmPlan& pl, const GemmParams& p, hipStream_t stre
   dim3 grid(pl.grid);
 #define NVFP4_KP(BM, NS, KW, BN) \
   hipLaunchKernelGGL((gemm_kp_kernel<BM, NS, KW, BN>), grid, dim3(KW * 64), 0, stream, p)
-  if (pl.kind == 1) {
+  if (pl.kind == 3) {
+    hipLaunchKernelGGL(gemm_lm_kernel, grid, dim3(256), 0, stream, p);
+  } else if (pl.kind == 1) {
     if (pl.bm == 16) NVFP4_KP(16, 5, 4, 128);
     else NVFP4_KP(32, 4, 4, 128);
   } else if (pl.kind == 2) {

@@ -93,6 +93,24 @@ def test_ragged_shapes(m, n, k):
     check_close(run_gemm(nv, x, qw, torch.bfloat16), y_ref, d, "bf16 %dx%dx%d" % (m, n, k))
 
 
+LARGE_M = [(256, 256, 64), (257, 300, 576), (300, 513, 1088), (511, 1024, 2048), (1000, 129, 4096)]
+
+
+@pytest.mark.parametrize("m,n,k", LARGE_M)
+def test_large_m_shapes(m, n, k):
+    """Row counts of 256 and more take the 256 x 256 tile path; ragged M, N
+    and one-step K included."""
+    nv = require_gpu()
+    key = m * 1000003 + n * 1009 + k
+    w = W.normal_bf16((n, k), 0.05, (79, key, 0))
+    x = W.normal_bf16((m, k), 1.0, (79, key, 1))
+    p, s, g = oracle_weight(w)
+    y_ref, d = oracle.gemm(x, p, s, g[0])
+    qw = to_qw(nv, p, s, g)
+    check_close(run_gemm(nv, x, qw, torch.float32), y_ref, d, "f32 %dx%dx%d" % (m, n, k))
+    check_close(run_gemm(nv, x, qw, torch.bfloat16), y_ref, d, "bf16 %dx%dx%d" % (m, n, k))
+
+
 @pytest.mark.parametrize("splitk", [1, 2, 3, 7], indirect=True)
 @pytest.mark.parametrize("m,n,k", [(16, 256, 1024), (3, 300, 1088), (64, 513, 960), (20, 64, 80)])
 def test_forced_split_k(splitk, m, n, k):

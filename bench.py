@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run five 1 GiB device-to-device copies (run under rocprofv3 "
                          "--pmc to calibrate FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--dense", nargs=3, type=int, metavar=("M", "N", "K"),
+                    help="only time one dense GEMM of this shape (e.g. to profile its kernel) "
+                         "and print one JSON line")
     ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV",
                                                            "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="write profiles/traffic.json from rocprofv3 counter CSVs of a bench "
@@ -247,6 +250,20 @@ def extras():
     return out
 
 
+def dense_only(m, n, k):
+    """One dense GEMM shape: 2 warm-up and 10 timed launches."""
+    import torch
+    import block_scaled_fp4_nibble_amd as nv
+    qw = nv.quantize(randn_bf16((n, k), 0.02, 400))
+    x = randn_bf16((m, k), 1.0, 401)
+    y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    ms = time_fn(lambda: nv.gemm(x, qw, out=y), 10, 2)
+    tf = 2 * m * n * k / (ms * 1e-3) / 1e12
+    print(json.dumps({"dense": [m, n, k], "ms": ms, "TFLOPS": tf,
+                      "frac_of_bf16_peak": tf / BF16_DENSE_PEAK_TFLOPS,
+                      "GBps": dense_bytes(m, n, k) / (ms * 1e-3) / 1e9}), flush=True)
+
+
 COPY_BYTES = 1 << 30
 
 
@@ -315,6 +332,9 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.dense:
+        dense_only(*args.dense)
         return
     launches = build_workload()
     step_flops = sum(L["flops"] for L in launches)

@@ -1065,6 +1065,7 @@ static int env_int(const char* name, int dflt) {
 //   3  large-M kernel, 256 x 256 tiles (dense products with at least
 //      kLmMinRows rows; NVFP4_LM=0 disables it)
 constexpr int kLmMinRows = 256;
+constexpr int kMinSplitStages = 12;
 
 static void choose_kernel(GemmPlan& pl, int64_t rows, bool grouped) {
   if (pl.fast && !grouped && rows >= kLmMinRows && env_int("NVFP4_LM", 1) != 0) {
@@ -1129,8 +1130,11 @@ GemmPlan plan_gemm(int64_t rows, int64_t num_experts, int64_t n, int64_t k, bool
   const int64_t tiles_est = grouped ? std::min<int64_t>(num_experts, rows) * pl.n_tiles
                                     : max_tiles;
   if (tiles_est < slots) {
+    // each split keeps at least kMinSplitStages K stages: below that the
+    // per-unit pipeline fill and the partial-tile hand-off cost more than the
+    // extra parallelism buys (measured on the decode shapes)
     int64_t want = (slots + tiles_est - 1) / tiles_est;
-    const int64_t kmax = std::max<int64_t>(1, k / (2 * kc));
+    const int64_t kmax = std::max<int64_t>(1, k / (kMinSplitStages * kc));
     splits = (int)std::min<int64_t>(want, kmax);
   }
   const int force_s = env_int("NVFP4_SPLITK", 0);

@@ -46,6 +46,8 @@
 //    tile's counter, and the last arrival sums the partials in split order
 //    (bitwise reproducible), resets the counter and writes the output.
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 #include <cstdlib>
 
 #include "device_common.hpp"
@@ -80,6 +82,11 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 __device__ __forceinline__ void lds_dma16(uint32_t lds, uint32_t voff, uint32_t soff,
                                           u32x4_t rsrc) {
+  // the descriptor is uniform; say so, so that it stays in SGPRs
+  rsrc = u32x4_t{(uint32_t)__builtin_amdgcn_readfirstlane(rsrc[0]),
+                 (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[1]),
+                 (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[2]),
+                 (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[3])};
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
@@ -115,10 +122,14 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total)
   return base + incl - v;
 }
 
-// Per-workgroup schedule: exclusive prefix of work units per expert (the
-// expert segments themselves are read from the offsets in device memory).
+// Per-workgroup schedule: the exclusive prefix of work units per expert lives
+// in dynamic LDS (4 (E + 1) bytes, sized at launch); the expert segments
+// themselves are read from the offsets in device memory.
+extern __shared__ int sched_units[];
+constexpr int kSchedLdsMax = 4 * (kMaxExperts + 1);
+inline int sched_lds_bytes(int64_t num_experts) { return (int)(4 * (num_experts + 1)); }
+
 struct Sched {
-  int units[kMaxExperts + 1];
   int tmp[16];
   int flag;
 };
@@ -159,10 +170,10 @@ __device__ int build_schedule(Sched& sc, const GemmParams& p) {
 #pragma unroll
   for (int t = 0; t < PER; ++t) {
     const int e = PER * tid + t;
-    if (e < E) sc.units[e] = ubase;
+    if (e < E) sched_units[e] = ubase;
     ubase += cnt[t];
   }
-  if (tid == 0) sc.units[E] = total_units;
+  if (tid == 0) sched_units[E] = total_units;
   __syncthreads();
   return total_units;
 }
@@ -191,19 +202,19 @@ __device__ __forceinline__ Unit decode_unit(const Sched& sc, const GemmParams& p
   int lo = 0, hi = p.num_experts;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (sc.units[mid] <= unit) lo = mid; else hi = mid;
+    if (sched_units[mid] <= unit) lo = mid; else hi = mid;
   }
   Unit u;
   u.e = __builtin_amdgcn_readfirstlane(lo);
   const int seg0 = __builtin_amdgcn_readfirstlane(seg_begin(p, u.e));
   const int seg1 = __builtin_amdgcn_readfirstlane(seg_begin(p, u.e + 1));
   const int mtiles = (seg1 - seg0 + BM - 1) / BM;
-  const int local = unit - sc.units[u.e];
+  const int local = unit - sched_units[u.e];
   const int mt = local % mtiles;
   const int rest = local / mtiles;
   u.ks = rest % p.splits;
   u.nt = rest / p.splits;
-  u.tile = sc.units[u.e] / p.splits + u.nt * mtiles + mt;
+  u.tile = sched_units[u.e] / p.splits + u.nt * mtiles + mt;
   u.row0 = seg0 + mt * BM;
   u.row_end = min(u.row0 + BM, seg1);
   u.k_beg = u.ks * p.k_split;
@@ -337,16 +348,24 @@ struct KpLayout {
   static constexpr int kWPerWave = BN / 16 / KW;    // 1 KB (16-row) weight loads per wave
   static constexpr int kXInstr = BM / 4;            // 1 KB (4-row) activation loads
   static constexpr int kXPerWave = kXInstr >= KW ? kXInstr / KW : 1;
-  static constexpr int kSInstr = BN / 32;           // 1 KB (32-row) scale window loads
   static constexpr int kLoadsPerStage = kWPerWave + kXPerWave;
-  static constexpr int kWinStages = 4;              // scale window = 4 stages = 512 K
-  static constexpr int kWinBytes = BN * 32;
+  // A scale window covers kWinStages stages (8 bytes per row each) and goes
+  // out just before its first stage, into the buffer of the window two back;
+  // that buffer is free once every wave has read that window's last stage,
+  // which holds when NSLOT <= kWinStages + 1.
+  static constexpr int kWinStages = NSLOT <= 3 ? 2 : 4;
+  static constexpr int kWinRow = 8 * kWinStages;    // window bytes per weight row
+  static constexpr int kWinBytes = BN * kWinRow;
+  static constexpr int kSInstr = kWinBytes / 1024;  // 1 KB scale window loads
   static constexpr int kSWin = NSLOT * kStage;
   static constexpr int kTotal = kSWin + 2 * kWinBytes;
-  static_assert(kWPerWave >= 1 && KW >= kSInstr, "load split");
+  static constexpr int kSPerWave = kSInstr >= KW ? kSInstr / KW : 1;
+  static_assert(kWPerWave >= 1 && kSInstr >= 1 && (kSInstr < KW || kSInstr % KW == 0),
+                "load split");
+  static_assert(NSLOT <= kWinStages + 1, "window buffers are reused in time");
   static_assert(kNJ % 2 == 0, "column tiles split between the K halves");
   static_assert(NSLOT >= 3 && NSLOT <= 5, "windows are issued one window ahead");
-  static_assert(kTotal + (int)sizeof(Sched) <= 160 * 1024, "LDS budget");
+  static_assert(kTotal + (int)sizeof(Sched) + kSchedLdsMax <= 160 * 1024, "LDS budget");
   static_assert(kTotal >= KW * (BM / 16) * (kNJ / 2) * 1024, "reduction buffer fits the ring");
 };
 
@@ -355,12 +374,12 @@ struct KpOffsets {
   uint32_t w[KpLayout<BM, 4, KW, BN>::kWPerWave];
   uint32_t x[KpLayout<BM, 4, KW, BN>::kXPerWave];
   int xk[KpLayout<BM, 4, KW, BN>::kXPerWave];
-  uint32_t s;
+  uint32_t s[2];
 };
 
-template <int BM, int KW, int BN>
+template <int BM, int NSLOT, int KW, int BN>
 __device__ __forceinline__ KpOffsets<BM, KW, BN> kp_offsets(int n0, int K, int wave, int lane) {
-  using L = KpLayout<BM, 4, KW, BN>;
+  using L = KpLayout<BM, NSLOT, KW, BN>;
   KpOffsets<BM, KW, BN> o;
   // weights: load t covers rows 16t..16t+15 (64 B each); slot s of row R
   // receives chunk s ^ ((R >> 2) & 3)
@@ -381,11 +400,15 @@ __device__ __forceinline__ KpOffsets<BM, KW, BN> kp_offsets(int n0, int K, int w
     o.x[tt] = (uint32_t)r * (uint32_t)(K * 2) + (uint32_t)(16 * g);
     o.xk[tt] = 8 * g;
   }
-  // scale window: 1 KB loads of 32 rows x 32 bytes, one per wave (waves
-  // beyond the load count repeat a load)
-  {
-    const int R = (wave % L::kSInstr) * 32 + (lane >> 1);
-    o.s = (uint32_t)(n0 + R) * (uint32_t)(K / 16) + (uint32_t)(16 * (lane & 1));
+  // scale window: 1 KB loads of 1024 / kWinRow rows, kSPerWave per wave
+  // (waves beyond the load count repeat a load)
+  static_assert(L::kSPerWave <= 2, "scale loads per wave");
+#pragma unroll
+  for (int tt = 0; tt < L::kSPerWave; ++tt) {
+    constexpr int LPR = L::kWinRow / 16;  // lanes per row
+    const int t = L::kSInstr >= KW ? wave * L::kSPerWave + tt : wave % L::kSInstr;
+    const int R = t * (64 / LPR) + lane / LPR;
+    o.s[tt] = (uint32_t)(n0 + R) * (uint32_t)(K / 16) + (uint32_t)(16 * (lane % LPR));
   }
   return o;
 }
@@ -407,12 +430,17 @@ __device__ __forceinline__ void kp_issue(uint32_t stage, u32x4_t rw, u32x4_t rx,
   }
 }
 
-// Issue the scale window [kw, kw + 512) of the unit (one 1 KB load per wave).
+// Issue the scale window [kw, kw + 128 kWinStages) of the unit (one 1 KB load
+// per wave).
 template <int BM, int NSLOT, int KW, int BN>
-__device__ __forceinline__ void kp_issue_scales(uint32_t slot, u32x4_t rs, uint32_t soff_lane,
-                                                int kw, int wave) {
+__device__ __forceinline__ void kp_issue_scales(uint32_t slot, u32x4_t rs,
+                                                const KpOffsets<BM, KW, BN>& o, int kw, int wave) {
   using L = KpLayout<BM, NSLOT, KW, BN>;
-  lds_dma16(slot + (wave % L::kSInstr) * 1024, soff_lane, (uint32_t)(kw / 16), rs);
+#pragma unroll
+  for (int tt = 0; tt < L::kSPerWave; ++tt) {
+    const int t = L::kSInstr >= KW ? wave * L::kSPerWave + tt : wave % L::kSInstr;
+    lds_dma16(slot + t * 1024, o.s[tt], (uint32_t)(kw / 16), rs);
+  }
 }
 
 // One stage's operands of one wave: per column tile j, 16 nibbles (two MFMA
@@ -422,13 +450,14 @@ template <int BM, int NJ>
 struct KpRegs {
   u32x2_t wd[NJ];
   uint32_t sc[NJ];
+  bool kv;  // the lane's scale block lies inside the unit's K range
   bf16x8_t a[2][BM / 16];
 };
 
 // Lane group q of wave half kp supplies K = 64 kp + 16 q + 8 i .. +7 of the
 // stage in MFMA step i: its 16 K are one scale block (block 4 kp + q of the
 // stage), 8 contiguous weight bytes and two 16-byte activation chunks.
-template <int BM, int NJ, int NFE, int BN>
+template <int BM, int NJ, int NFE, int BN, int WS>
 __device__ __forceinline__ void kp_read(KpRegs<BM, NJ>& r, const uint8_t* stage,
                                         const uint8_t* swin, int sub, bool kvalid, int kp,
                                         int ch, int lane) {
@@ -439,9 +468,9 @@ __device__ __forceinline__ void kp_read(KpRegs<BM, NJ>& r, const uint8_t* stage,
     const int R = ch * (NJ * 16) + j * 16 + r16;
     r.wd[j] = *reinterpret_cast<const u32x2_t*>(stage + R * 64 + 16 * (cw ^ ((R >> 2) & 3)) +
                                                 8 * (q & 1));
-    const uint32_t s = swin[R * 32 + 8 * sub + 4 * kp + q];
-    r.sc[j] = kvalid ? s : 0u;
+    r.sc[j] = swin[R * (8 * WS) + 8 * sub + 4 * kp + q];
   }
+  r.kv = kvalid;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -456,7 +485,7 @@ template <int BM, int NJ, int NFE>
 __device__ __forceinline__ void kp_mma(f32x4_t (&acc)[BM / 16][NJ], const KpRegs<BM, NJ>& r) {
   float scl[NJ];
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) scl[j] = decode_e4m3<0>(r.sc[j]);
+  for (int j = 0; j < NJ; ++j) scl[j] = r.kv ? decode_e4m3<0>(r.sc[j]) : 0.f;
   constexpr int T = 2 * NJ;
   bf16x8_t b[2];
   b[0] = dequant8(r.wd[0][0], scl[0]);
@@ -476,11 +505,12 @@ __device__ __forceinline__ void kp_mma(f32x4_t (&acc)[BM / 16][NJ], const KpRegs
 // The K loop of one unit, for tiles whose rows fill NFE of the BM / 16 row
 // fragments (fragments past NFE are pure padding and are skipped).
 //
-// Per unit (per wave, in issue order): scale window 0, stages 0..D-1
-// (D = NSLOT - 1).  Iteration c waits until stage c + 1 has landed, passes the
-// barrier (every wave is then done with stage c - 1, whose slot is refilled),
-// issues scale window c/4 + 1 when c % 4 == 0 and stage c + D, reads stage
-// c + 1 into registers and multiplies out stage c.
+// Per unit (per wave, in issue order): stages 0 .. NSLOT-1, each preceded by
+// the scale window that starts at it (every WS-th stage).  Iteration c waits
+// until stage c + 1 has landed and passes the barrier: every wave has then
+// read stage c into registers (in iteration c - 1, or before the loop when
+// c = 0), so stage c's slot takes stage c + NSLOT.  It then reads stage c + 1
+// into registers and multiplies out stage c.
 template <int BM, int NSLOT, int KW, int BN, int NFE>
 __device__ __forceinline__ void kp_kloop(f32x4_t (&acc)[BM / 16][2 * BN / KW / 16],
                                          uint8_t* ring, const Unit& u, u32x4_t rw, u32x4_t rs,
@@ -488,42 +518,45 @@ __device__ __forceinline__ void kp_kloop(f32x4_t (&acc)[BM / 16][2 * BN / KW / 1
                                          int ch, int wave, int lane) {
   using L = KpLayout<BM, NSLOT, KW, BN>;
   constexpr int NJ = L::kNJ;
-  constexpr int D = NSLOT - 1;
+  constexpr int D = NSLOT;  // stages in flight after an iteration's issue
   constexpr int WS = L::kWinStages;
   constexpr int LS = L::kLoadsPerStage;
+  constexpr int SPW = L::kSPerWave;
   const int q = lane >> 4;
   const uint32_t ring0 = lds_addr(ring);
   const int nch = (u.k_end - u.k_beg + kRingKC - 1) / kRingKC;
-  const int nwin = (nch + WS - 1) / WS;
   // K validity of this lane's scale block in stage c
   auto kvalid = [&](int c) { return u.k_beg + c * kRingKC + 64 * kp + 16 * q < u.k_end; };
-  kp_issue_scales<BM, NSLOT, KW, BN>(ring0 + L::kSWin, rs, off.s, u.k_beg, wave);
-  for (int s = 0; s < D && s < nch; ++s)
-    kp_issue<BM, NSLOT, KW, BN>(ring0 + s * L::kStage, rw, rx, off, u.k_beg + s * kRingKC,
-                                u.k_end, wave);
-  wait_vmcnt(LS * (min(D - 1, nch - 1)));
+  auto issue_stage = [&](int st) {
+    if (st % WS == 0)
+      kp_issue_scales<BM, NSLOT, KW, BN>(ring0 + L::kSWin + ((st / WS) & 1) * L::kWinBytes, rs,
+                                         off, u.k_beg + st * kRingKC, wave);
+    kp_issue<BM, NSLOT, KW, BN>(ring0 + (st % NSLOT) * L::kStage, rw, rx, off,
+                                u.k_beg + st * kRingKC, u.k_end, wave);
+  };
+  // loads this wave issued after those of stage lo, through stage hi
+  auto loads_after = [&](int lo, int hi) {
+    int n = 0;
+#pragma unroll
+    for (int i = 1; i < D; ++i)
+      if (lo + i <= hi) n += LS + ((lo + i) % WS == 0 ? SPW : 0);
+    return n;
+  };
+  for (int st = 0; st < D && st < nch; ++st) issue_stage(st);
+  wait_vmcnt(loads_after(0, min(D, nch) - 1));
   __syncthreads();
   KpRegs<BM, NJ> ra, rb;
-  kp_read<BM, NJ, NFE, BN>(ra, ring, ring + L::kSWin, 0, kvalid(0), kp, ch, lane);
+  kp_read<BM, NJ, NFE, BN, WS>(ra, ring, ring + L::kSWin, 0, kvalid(0), kp, ch, lane);
 
   auto step = [&](int c, const KpRegs<BM, NJ>& cur, KpRegs<BM, NJ>& nxt) {
     if (c + 1 < nch) {
-      // loads issued after stage c + 1: stages c+2 .. c+D-1 and the windows
-      // issued at iterations c+2-D .. c-1
-      int after = LS * max(0, min(c + D - 1, nch - 1) - (c + 1));
-      for (int i = max(0, c + 2 - D); i < c; ++i)
-        after += (i % WS == 0 && i / WS + 1 < nwin) ? 1 : 0;
-      wait_vmcnt(after);
+      // stages c + 1 .. min(c + D - 1, nch - 1) are in flight
+      wait_vmcnt(loads_after(c + 1, min(c + D - 1, nch - 1)));
       __syncthreads();
-      if (c % WS == 0 && c / WS + 1 < nwin)
-        kp_issue_scales<BM, NSLOT, KW, BN>(ring0 + L::kSWin + ((c / WS + 1) & 1) * L::kWinBytes,
-                                           rs, off.s, u.k_beg + (c / WS + 1) * WS * kRingKC, wave);
-      if (c + D < nch)
-        kp_issue<BM, NSLOT, KW, BN>(ring0 + ((c + D) % NSLOT) * L::kStage, rw, rx, off,
-                                    u.k_beg + (c + D) * kRingKC, u.k_end, wave);
-      kp_read<BM, NJ, NFE, BN>(nxt, ring + ((c + 1) % NSLOT) * L::kStage,
-                               ring + L::kSWin + (((c + 1) / WS) & 1) * L::kWinBytes,
-                               (c + 1) % WS, kvalid(c + 1), kp, ch, lane);
+      if (c + D < nch) issue_stage(c + D);
+      kp_read<BM, NJ, NFE, BN, WS>(nxt, ring + ((c + 1) % NSLOT) * L::kStage,
+                                   ring + L::kSWin + (((c + 1) / WS) & 1) * L::kWinBytes,
+                                   (c + 1) % WS, kvalid(c + 1), kp, ch, lane);
     }
     kp_mma<BM, NJ, NFE>(acc, cur);
   };
@@ -558,7 +591,7 @@ __global__ __launch_bounds__(KW * 64) void gemm_kp_kernel(GemmParams p) {
         rsrc_words(p.s + (int64_t)u.e * N * (K / 16), (uint32_t)N * (uint32_t)(K / 16));
     const u32x4_t rx =
         rsrc_words(p.x + (int64_t)u.row0 * K, (uint32_t)(u.row_end - u.row0) * (uint32_t)(K * 2));
-    const KpOffsets<BM, KW, BN> off = kp_offsets<BM, KW, BN>(n0, K, wave, lane);
+    const KpOffsets<BM, KW, BN> off = kp_offsets<BM, NSLOT, KW, BN>(n0, K, wave, lane);
     const float gv = p.g[u.e];  // issued now, first used in the epilogue
     // 16-row fragments holding rows of this tile (the rest is padding)
     const int nf = min(NF, (u.row_end - u.row0 + 15) / 16);
@@ -1043,9 +1076,10 @@ hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t stream) {
 }
 
 template <typename KernelT>
-static int occupancy_of(KernelT kernel, int threads) {
+static int occupancy_of(KernelT kernel, int threads, int dyn_lds) {
   int v = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, kernel, threads, 0) != hipSuccess || v < 1)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, kernel, threads, dyn_lds) != hipSuccess ||
+      v < 1)
     v = 1;
   return v;
 }
@@ -1079,25 +1113,37 @@ static void choose_kernel(GemmPlan& pl, int64_t rows, bool grouped) {
   }
 }
 
+// Resident workgroups per CU of the chosen kernel with its dynamic LDS
+// (cached per kernel and 256-byte step of the schedule size).
 static int occupancy_for(const GemmPlan& pl) {
-  static int cache[4][3] = {{-1, -1, -1}, {-1, -1, -1}, {-1, -1, -1}, {-1, -1, -1}};
+  constexpr int kSteps = kSchedLdsMax / 256 + 2;
+  static std::atomic<int> cache[4][3][kSteps];
+  static std::once_flag once;
+  std::call_once(once, [] {
+    for (auto& a : cache)
+      for (auto& b : a)
+        for (auto& c : b) c.store(-1);
+  });
   const int bi = pl.bm == 16 ? 0 : (pl.bm == 32 ? 1 : 2);
-  int& c = cache[pl.kind][bi];
+  const int dyn = pl.dyn_lds;
+  std::atomic<int>& slot = cache[pl.kind][bi][std::min(kSteps - 1, (dyn + 255) / 256)];
+  int c = slot.load();
   if (c < 0) {
     if (pl.kind == 0) {
-      c = pl.bm == 16 ? occupancy_of(gemm_reg_kernel<16>, kRegThreads)
-          : pl.bm == 32 ? occupancy_of(gemm_reg_kernel<32>, kRegThreads)
-                        : occupancy_of(gemm_reg_kernel<64>, kRegThreads);
+      c = pl.bm == 16 ? occupancy_of(gemm_reg_kernel<16>, kRegThreads, dyn)
+          : pl.bm == 32 ? occupancy_of(gemm_reg_kernel<32>, kRegThreads, dyn)
+                        : occupancy_of(gemm_reg_kernel<64>, kRegThreads, dyn);
     } else if (pl.kind == 3) {
-      c = occupancy_of(gemm_lm_kernel, 256);
+      c = occupancy_of(gemm_lm_kernel, 256, dyn);
     } else if (pl.kind == 1) {
-      c = pl.bm == 16 ? occupancy_of(gemm_kp_kernel<16, 5, 4, 128>, 256)
-                      : occupancy_of(gemm_kp_kernel<32, 4, 4, 128>, 256);
+      c = pl.bm == 16 ? occupancy_of(gemm_kp_kernel<16, 5, 4, 128>, 256, dyn)
+                      : occupancy_of(gemm_kp_kernel<32, 4, 4, 128>, 256, dyn);
     } else {
-      c = pl.bm == 16 ? occupancy_of(gemm_kp_kernel<16, 5, 8, 256>, 512)
-          : pl.bm == 32 ? occupancy_of(gemm_kp_kernel<32, 5, 8, 256>, 512)
-                        : occupancy_of(gemm_kp_kernel<64, 4, 8, 256>, 512);
+      c = pl.bm == 16 ? occupancy_of(gemm_kp_kernel<16, 5, 8, 256>, 512, dyn)
+          : pl.bm == 32 ? occupancy_of(gemm_kp_kernel<32, 5, 8, 256>, 512, dyn)
+                        : occupancy_of(gemm_kp_kernel<64, 4, 8, 256>, 512, dyn);
     }
+    slot.store(c);
   }
   return c;
 }
@@ -1114,6 +1160,8 @@ GemmPlan plan_gemm(int64_t rows, int64_t num_experts, int64_t n, int64_t k, bool
   if (force_bm == 16 || force_bm == 32 || force_bm == 64) bm = force_bm;
   pl.bm = bm;
   choose_kernel(pl, rows, grouped);
+  // the large-M kernel keeps no schedule (dense only)
+  pl.dyn_lds = pl.kind == 3 ? 0 : sched_lds_bytes(grouped ? num_experts : 1);
   bm = pl.bm;
   pl.n_tiles = (int)((n + pl.bn - 1) / pl.bn);
   // Upper bound on output tiles: each non-empty expert adds at most one
@@ -1157,7 +1205,7 @@ GemmPlan plan_gemm(int64_t rows, int64_t num_experts, int64_t n, int64_t k, bool
 hipError_t launch_gemm(const GemmPlan& pl, const GemmParams& p, hipStream_t stream) {
   dim3 grid(pl.grid);
 #define NVFP4_KP(BM, NS, KW, BN) \
-  hipLaunchKernelGGL((gemm_kp_kernel<BM, NS, KW, BN>), grid, dim3(KW * 64), 0, stream, p)
+  hipLaunchKernelGGL((gemm_kp_kernel<BM, NS, KW, BN>), grid, dim3(KW * 64), pl.dyn_lds, stream, p)
   if (pl.kind == 3) {
     hipLaunchKernelGGL(gemm_lm_kernel, grid, dim3(256), 0, stream, p);
   } else if (pl.kind == 1) {
@@ -1169,9 +1217,10 @@ hipError_t launch_gemm(const GemmPlan& pl, const GemmParams& p, hipStream_t stre
     else NVFP4_KP(64, 4, 8, 256);
   } else {
     dim3 block(kRegThreads);
-    if (pl.bm == 16) hipLaunchKernelGGL(gemm_reg_kernel<16>, grid, block, 0, stream, p);
-    else if (pl.bm == 32) hipLaunchKernelGGL(gemm_reg_kernel<32>, grid, block, 0, stream, p);
-    else hipLaunchKernelGGL(gemm_reg_kernel<64>, grid, block, 0, stream, p);
+    if (pl.bm == 16) hipLaunchKernelGGL(gemm_reg_kernel<16>, grid, block, pl.dyn_lds, stream, p);
+    else if (pl.bm == 32)
+      hipLaunchKernelGGL(gemm_reg_kernel<32>, grid, block, pl.dyn_lds, stream, p);
+    else hipLaunchKernelGGL(gemm_reg_kernel<64>, grid, block, pl.dyn_lds, stream, p);
   }
 #undef NVFP4_KP
   return hipGetLastError();

@@ -46,6 +46,7 @@ struct GemmPlan {
   int kind;      // kernel configuration (see plan_gemm)
   int bn;        // columns per tile: 128 or 256
   int nslot;     // LDS ring slots of the K-phase kernel
+  int dyn_lds;   // dynamic LDS bytes of the launch (the per-expert unit prefix)
   int splits;
   int k_split;
   int n_tiles;

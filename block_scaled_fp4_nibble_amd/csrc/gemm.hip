@@ -65,6 +65,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 }
 constexpr uint32_t kOffNone = 0x80000000u;  // beyond every resource: loads return 0
 
+// Cache policy of buffer accesses that must be coherent across the XCDs'
+// L2 caches (device scope): the sc1 bit.  Such stores write through to
+// memory and such loads do not hit lines another XCD may have left stale.
+constexpr int kCpolDevice = 16;
+
 // Direct global -> LDS loads (buffer_load ... lds): lane l writes its bytes
 // at M0 + l * size.  They are issued from inline assembly so that the
 // compiler does not treat every later LDS read as a possible alias of an
@@ -234,37 +239,66 @@ __device__ __forceinline__ bool finish_tile(f32x4_t (&acc)[NF][NW], const GemmPa
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = p.splits;
   if (S > 1) {
-    float* part = p.partials + (int64_t)u.tile * S * (BM * BN);
+    // Hand-off between the splits of a tile, which may run on different XCDs
+    // (each with its own L2).  The partials are written and read with
+    // device-scope accesses, which go past the non-coherent L2, and each
+    // thread waits for its stores to complete before the barrier that
+    // precedes the arrival count; so no whole-L2 writeback or invalidate
+    // (what a device-scope fence costs) is needed.
+    const __amdgpu_buffer_rsrc_t part =
+        make_rsrc(p.partials + (int64_t)u.tile * S * (BM * BN), (uint32_t)(S * BM * BN * 4));
+    // byte offset of this lane's accumulator tile (f, j) in split s
+    auto poff = [&](int s, int f, int j) {
+      return (uint32_t)((s * (BM * BN) + (((wave * NF + f) * NW + j) * kWave + lane) * 4) * 4);
+    };
 #pragma unroll
     for (int f = 0; f < NF; ++f)
 #pragma unroll
       for (int j = 0; j < NW; ++j)
-        *reinterpret_cast<f32x4_t*>(part + (int64_t)u.ks * (BM * BN) +
-                                    (((wave * NF + f) * NW + j) * kWave + lane) * 4) = acc[f][j];
-    fence_release_agent();
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, acc[f][j]), part,
+                                               poff(u.ks, f, j), 0, kCpolDevice);
+    __builtin_amdgcn_s_waitcnt(0);  // every counter at zero: the stores have completed
     __syncthreads();
     if (tid == 0) {
-      const uint32_t old = atomicAdd(&p.counters[u.tile], 1u);
+      const uint32_t old =
+          __hip_atomic_fetch_add(&p.counters[u.tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       sc.flag = (old == (uint32_t)(S - 1));
     }
     __syncthreads();
     if (!sc.flag) return false;
-    fence_acquire_agent();
+    // Sum the partials in split order.  U splits are loaded before any is
+    // added, so about 8 independent loads are in flight instead of one.
+    constexpr int U = NF * NW >= 8 ? 1 : 8 / (NF * NW);
+    f32x4_t sum[NF][NW];
+    for (int s0 = 0; s0 < S; s0 += U) {
+      f32x4_t v[U][NF][NW];
+#pragma unroll
+      for (int i = 0; i < U; ++i) {
+        const int s = s0 + i;
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+#pragma unroll
+          for (int j = 0; j < NW; ++j)
+            v[i][f][j] = (s >= S || s == u.ks)
+                             ? acc[f][j]
+                             : __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                               part, poff(s, f, j), 0, kCpolDevice));
+      }
+#pragma unroll
+      for (int i = 0; i < U; ++i) {
+        if (s0 + i >= S) break;
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+#pragma unroll
+          for (int j = 0; j < NW; ++j)
+            sum[f][j] = (s0 + i == 0) ? v[i][f][j] : sum[f][j] + v[i][f][j];
+      }
+    }
 #pragma unroll
     for (int f = 0; f < NF; ++f)
 #pragma unroll
-      for (int j = 0; j < NW; ++j) {
-        f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < S; ++s) {
-          f32x4_t v = (s == u.ks) ? acc[f][j]
-                                  : __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(
-                                        part + (int64_t)s * (BM * BN) +
-                                        (((wave * NF + f) * NW + j) * kWave + lane) * 4));
-          sum = (s == 0) ? v : sum + v;
-        }
-        acc[f][j] = sum;
-      }
-    if (tid == 0) p.counters[u.tile] = 0u;
+      for (int j = 0; j < NW; ++j) acc[f][j] = sum[f][j];
+    if (tid == 0) __hip_atomic_store(&p.counters[u.tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   const int q = lane >> 4, r16 = lane & 15;
 #pragma unroll
@@ -1099,7 +1133,7 @@ static int env_int(const char* name, int dflt) {
 //   3  large-M kernel, 256 x 256 tiles (dense products with at least
 //      kLmMinRows rows; NVFP4_LM=0 disables it)
 constexpr int kLmMinRows = 256;
-constexpr int kMinSplitStages = 12;
+constexpr int kMinSplitStages = 7;
 
 static void choose_kernel(GemmPlan& pl, int64_t rows, bool grouped) {
   if (pl.fast && !grouped && rows >= kLmMinRows && env_int("NVFP4_LM", 1) != 0) {

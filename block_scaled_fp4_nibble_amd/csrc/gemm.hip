@@ -46,6 +46,7 @@
 //    tile's counter, and the last arrival sums the partials in split order
 //    (bitwise reproducible), resets the counter and writes the output.
 #include <algorithm>
+#include <type_traits>
 #include <atomic>
 #include <mutex>
 #include <cstdlib>
@@ -347,6 +348,13 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 #undef NVFP4_VMCNT
 }
 
+// s_waitcnt vmcnt(N) for a compile-time N.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_c() {
+  static_assert(N >= 0 && N < 63, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // ---- K-phase kernel (k % 64 == 0) ----------------------------------------------
 //
 // A work unit is (expert, row tile of BM rows, column tile of BN = 128 or 256
@@ -447,7 +455,9 @@ __device__ __forceinline__ KpOffsets<BM, KW, BN> kp_offsets(int n0, int K, int w
   return o;
 }
 
-template <int BM, int NSLOT, int KW, int BN>
+// TAIL: the stage may reach past the end of the unit's K range (only its
+// last stage can).
+template <int BM, int NSLOT, int KW, int BN, bool TAIL = true>
 __device__ __forceinline__ void kp_issue(uint32_t stage, u32x4_t rw, u32x4_t rx,
                                          const KpOffsets<BM, KW, BN>& o, int kc, int k_end,
                                          int wave) {
@@ -455,7 +465,7 @@ __device__ __forceinline__ void kp_issue(uint32_t stage, u32x4_t rw, u32x4_t rx,
 #pragma unroll
   for (int tt = 0; tt < L::kWPerWave; ++tt)
     lds_dma16(stage + L::kW + (wave * L::kWPerWave + tt) * 1024, o.w[tt], (uint32_t)(kc / 2), rw);
-  const bool tail = kc + kRingKC > k_end;
+  const bool tail = TAIL && kc + kRingKC > k_end;
 #pragma unroll
   for (int tt = 0; tt < L::kXPerWave; ++tt) {
     const int t = L::kXInstr >= KW ? wave * L::kXPerWave + tt : wave % L::kXInstr;
@@ -545,6 +555,10 @@ __device__ __forceinline__ void kp_mma(f32x4_t (&acc)[BM / 16][NJ], const KpRegs
 // read stage c into registers (in iteration c - 1, or before the loop when
 // c = 0), so stage c's slot takes stage c + NSLOT.  It then reads stage c + 1
 // into registers and multiplies out stage c.
+//
+// While the stage issued is neither past the end nor the unit's last one,
+// the iterations run in blocks of WS whose waits, window issues and K checks
+// are compile-time constants; the remaining iterations take the general path.
 template <int BM, int NSLOT, int KW, int BN, int NFE>
 __device__ __forceinline__ void kp_kloop(f32x4_t (&acc)[BM / 16][2 * BN / KW / 16],
                                          uint8_t* ring, const Unit& u, u32x4_t rw, u32x4_t rs,
@@ -556,6 +570,7 @@ __device__ __forceinline__ void kp_kloop(f32x4_t (&acc)[BM / 16][2 * BN / KW / 1
   constexpr int WS = L::kWinStages;
   constexpr int LS = L::kLoadsPerStage;
   constexpr int SPW = L::kSPerWave;
+  static_assert(WS % 2 == 0, "blocks keep the register double buffer in phase");
   const int q = lane >> 4;
   const uint32_t ring0 = lds_addr(ring);
   const int nch = (u.k_end - u.k_beg + kRingKC - 1) / kRingKC;
@@ -582,6 +597,29 @@ __device__ __forceinline__ void kp_kloop(f32x4_t (&acc)[BM / 16][2 * BN / KW / 1
   KpRegs<BM, NJ> ra, rb;
   kp_read<BM, NJ, NFE, BN, WS>(ra, ring, ring + L::kSWin, 0, kvalid(0), kp, ch, lane);
 
+  // iteration c = c0 + T of a steady block (c0 % WS == 0): stages c + 1 ..
+  // c + D - 1 are in flight and full, stage c + D is full and not the last
+  auto steady = [&](auto tc, int c0, const KpRegs<BM, NJ>& cur, KpRegs<BM, NJ>& nxt) {
+    constexpr int T = decltype(tc)::value;
+    constexpr int kAfter = [] {
+      int n = 0;
+      for (int i = 2; i < D; ++i) n += LS + ((T + i) % WS == 0 ? SPW : 0);
+      return n;
+    }();
+    const int c = c0 + T;
+    wait_vmcnt_c<kAfter>();
+    __syncthreads();
+    if constexpr ((T + D) % WS == 0)
+      kp_issue_scales<BM, NSLOT, KW, BN>(
+          ring0 + L::kSWin + (((c + D) / WS) & 1) * L::kWinBytes, rs, off,
+          u.k_beg + (c + D) * kRingKC, wave);
+    kp_issue<BM, NSLOT, KW, BN, false>(ring0 + ((c + D) % NSLOT) * L::kStage, rw, rx, off,
+                                       u.k_beg + (c + D) * kRingKC, u.k_end, wave);
+    kp_read<BM, NJ, NFE, BN, WS>(nxt, ring + ((c + 1) % NSLOT) * L::kStage,
+                                 ring + L::kSWin + (((c + 1) / WS) & 1) * L::kWinBytes,
+                                 (T + 1) % WS, true, kp, ch, lane);
+    kp_mma<BM, NJ, NFE>(acc, cur);
+  };
   auto step = [&](int c, const KpRegs<BM, NJ>& cur, KpRegs<BM, NJ>& nxt) {
     if (c + 1 < nch) {
       // stages c + 1 .. min(c + D - 1, nch - 1) are in flight
@@ -594,7 +632,16 @@ __device__ __forceinline__ void kp_kloop(f32x4_t (&acc)[BM / 16][2 * BN / KW / 1
     }
     kp_mma<BM, NJ, NFE>(acc, cur);
   };
-  for (int c = 0; c < nch; c += 2) {
+  int c = 0;
+  for (; c + WS + D < nch; c += WS) {
+    steady(std::integral_constant<int, 0>{}, c, ra, rb);
+    steady(std::integral_constant<int, 1>{}, c, rb, ra);
+    if constexpr (WS == 4) {
+      steady(std::integral_constant<int, 2>{}, c, ra, rb);
+      steady(std::integral_constant<int, 3>{}, c, rb, ra);
+    }
+  }
+  for (; c < nch; c += 2) {
     step(c, ra, rb);
     if (c + 1 < nch) step(c + 1, rb, ra);
   }

@@ -127,6 +127,23 @@ def test_forced_split_k(splitk, m, n, k):
     assert np.array_equal(host(y1).view(np.uint32), host(y2).view(np.uint32)), "not reproducible"
 
 
+@pytest.mark.parametrize("splitk", [9, 28, 56], indirect=True)
+@pytest.mark.parametrize("m", [1, 64])
+def test_decode_deep_split(decode_weight, splitk, m):
+    # many K splits per output tile (down to one 128-deep stage each): the
+    # partial-tile hand-off between workgroups on different XCDs, summed in
+    # split order
+    nv = require_gpu()
+    p, s, g = decode_weight
+    x = W.decode_act(m)
+    y_ref, d = oracle.gemm(x, p, s, g[0])
+    qw = to_qw(nv, p, s, g)
+    y1 = run_gemm(nv, x, qw, torch.float32)
+    check_close(y1, y_ref, d, "decode m=%d split %d" % (m, splitk))
+    y2 = run_gemm(nv, x, qw, torch.float32)
+    assert np.array_equal(host(y1).view(np.uint32), host(y2).view(np.uint32)), "not reproducible"
+
+
 def test_default_schedule_reproducible(decode_weight):
     nv = require_gpu()
     p, s, g = decode_weight

@@ -6,6 +6,8 @@ collapsing: ~16 and ~64 tokens per expert ("The FP4 Frontier", section "The
 Context").  Full-size workloads are checked on sampled outputs plus the
 property that every routed row is written; reduced sizes are checked in
 full."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -59,6 +61,33 @@ def test_small_full(counts, n, k, out_dtype):
     y_ref, d = oracle.grouped_gemm(x, off, p, s, g)
     y = run_grouped(nv, x, off, to_qw(nv, p, s, g), out_dtype)
     check_close(y, y_ref, d, "grouped %s n=%d k=%d" % (counts, n, k))
+
+
+@pytest.mark.parametrize("splits", [2, 5, 12])
+@pytest.mark.parametrize("counts,n,k", [
+    ([3, 0, 17, 1, 0, 40, 64, 65], 300, 1536),
+    ([70, 0, 5, 33], 513, 2048),
+])
+def test_forced_split_k(counts, n, k, splits):
+    # K split across workgroups inside a grouped launch: per-expert tile
+    # numbering of the partial-tile hand-off, empty experts, ragged tails
+    nv = require_gpu()
+    x, off, w = small_case(counts, n, k, seed=sum(counts) * 13 + n + k + splits)
+    p, s, g = oracle_weights(w)
+    y_ref, d = oracle.grouped_gemm(x, off, p, s, g)
+    qw = to_qw(nv, p, s, g)
+    old = os.environ.get("NVFP4_SPLITK")
+    os.environ["NVFP4_SPLITK"] = str(splits)
+    try:
+        y1 = run_grouped(nv, x, off, qw, torch.float32)
+        y2 = run_grouped(nv, x, off, qw, torch.float32)
+    finally:
+        if old is None:
+            os.environ.pop("NVFP4_SPLITK", None)
+        else:
+            os.environ["NVFP4_SPLITK"] = old
+    check_close(y1, y_ref, d, "grouped split %d %s n=%d k=%d" % (splits, counts, n, k))
+    assert np.array_equal(host(y1).view(np.uint32), host(y2).view(np.uint32)), "not reproducible"
 
 
 def _sampled_check(nv, x, r, p, s, g, out_dtype, seed, count=3000):

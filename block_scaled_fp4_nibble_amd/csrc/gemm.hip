@@ -733,14 +733,16 @@ __global__ __launch_bounds__(KW * 64) void gemm_kp_kernel(GemmParams p) {
 //
 // For a dense product with at least a few hundred rows the weight tile is
 // worth dequantizing once into LDS and sharing across a large row tile: a
-// 256 x 256 output tile per workgroup of 4 waves (one per SIMD), each wave
-// a 128 x 128 quadrant of 4 x 4 v_mfma_f32_32x32x16_bf16 tiles (FP32
-// accumulators in AGPRs).  K advances in 64-wide steps through a 3-stage LDS
-// ring holding, per step, the activation tile (256 rows x 128 B) and the
-// packed weight tile (256 rows x 32 B); block scales arrive in windows of 4
-// steps (256 rows x 16 B).  Per step each wave reads its A and B fragments
-// from LDS, runs 64 MFMAs, and after a barrier dequantizes 64 weight rows of
-// the next step into the shared BF16 weight tile (256 rows x 128 B).
+// 256 x 256 output tile per workgroup of 8 waves, each wave a 128 x 64 block
+// of 4 x 2 v_mfma_f32_32x32x16_bf16 tiles (FP32 accumulators).  Two waves
+// share each SIMD, so one wave's dequantization, LDS and load-issue work can
+// run while the other's MFMAs occupy the matrix pipeline.  K advances in
+// 64-wide steps through a 3-stage LDS ring holding, per step, the
+// activation tile (256 rows x 128 B) and the packed weight tile (256 rows x
+// 32 B); block scales arrive in windows of 4 steps (256 rows x 16 B).  Per
+// step each wave reads its A and B fragments from LDS, runs 32 MFMAs, and
+// after a barrier writes its 32 weight rows of the next step, dequantized
+// between those MFMAs, into the shared BF16 weight tile (256 rows x 128 B).
 //
 // LDS rows of the activation and BF16 weight tiles keep their 16-byte
 // chunk c in slot c ^ ((r >> 1) & 7), so the 32-row fragment reads and the
@@ -748,6 +750,7 @@ __global__ __launch_bounds__(KW * 64) void gemm_kp_kernel(GemmParams p) {
 constexpr int kLmBM = 256, kLmBN = 256, kLmBK = 64;
 
 struct LmLayout {
+  static constexpr int kWaves = 8;
   static constexpr int kXStage = kLmBM * kLmBK * 2;          // 32 KB
   static constexpr int kWpStage = kLmBN * kLmBK / 2;         // 8 KB
   static constexpr int kStage = kXStage + kWpStage;
@@ -756,10 +759,12 @@ struct LmLayout {
   static constexpr int kWin = kWbf + kLmBN * kLmBK * 2;      // 2 scale windows of 4 KB
   static constexpr int kWinBytes = kLmBN * 16;
   static constexpr int kTotal = kWin + 2 * kWinBytes;
-  static constexpr int kXLoads = kXStage / 1024 / 4;         // per wave per step: 8
-  static constexpr int kWpLoads = kWpStage / 1024 / 4;       // per wave per step: 2
+  static constexpr int kXLoads = kXStage / 1024 / kWaves;    // per wave per step: 4
+  static constexpr int kWpLoads = kWpStage / 1024 / kWaves;  // per wave per step: 1
+  static constexpr int kWinLoads = kWinBytes / 1024;         // waves 0..3, one each
   static constexpr int kLoadsPerStage = kXLoads + kWpLoads;
   static_assert(kTotal <= 160 * 1024, "LDS budget");
+  static_assert(kXLoads >= 1 && kWpLoads >= 1 && kWinLoads <= kWaves, "load split");
 };
 
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
@@ -788,8 +793,8 @@ __device__ __forceinline__ LmOffsets lm_offsets(int K, int wave, int lane) {
     const int r = (wave * LmLayout::kWpLoads + tt) * 32 + (lane >> 1);
     o.wp[tt] = (uint32_t)r * (uint32_t)(K / 2) + (uint32_t)(16 * (lane & 1));
   }
-  // scale window: wave w loads rows 64w..64w+63, 16 B (256 K) each
-  o.s = (uint32_t)(wave * 64 + lane) * (uint32_t)(K / 16);
+  // scale window: wave w < 4 loads rows 64w..64w+63, 16 B (256 K) each
+  o.s = (uint32_t)((wave & 3) * 64 + lane) * (uint32_t)(K / 16);
   return o;
 }
 
@@ -797,7 +802,7 @@ __device__ __forceinline__ void lm_issue(uint32_t ring0, int step, u32x4_t rx, u
                                          u32x4_t rs, const LmOffsets& o, int wave) {
   // order: scale window (with the first step it covers), packed weights,
   // activations -- the weights of a step are needed one step earlier
-  if (step % 4 == 0)
+  if (step % 4 == 0 && wave < LmLayout::kWinLoads)
     lds_dma16(ring0 + LmLayout::kWin + ((step / 4) & 1) * LmLayout::kWinBytes + wave * 1024, o.s,
               (uint32_t)(step * kLmBK / 16), rs);
   const uint32_t st = ring0 + (step % LmLayout::kStages) * LmLayout::kStage;
@@ -811,87 +816,76 @@ __device__ __forceinline__ void lm_issue(uint32_t ring0, int step, u32x4_t rx, u
               rx);
 }
 
-// One lane's share of a weight step: row 64 wave + lane, 64 K = 8 dwords of
-// nibbles and the row's 4 block scales of the step.
+// One lane's share of a weight step: half h = lane % 2 (32 K) of row
+// 32 wave + lane / 2, as 4 dwords of nibbles and the row's 4 block scales of
+// the step shifted so that the lane's two are in bytes 0 and 1 (decoded
+// where they are used, so the LDS read is not waited for early).
 struct LmWp {
-  uint32_t d[8];
-  float sv[4];
+  uint32_t d[4];
+  uint32_t sc;
 };
 
 __device__ __forceinline__ void lm_read_wp(LmWp& w, const uint8_t* ring, int step, int wave, int lane) {
-  const int r = wave * 64 + lane;
+  const int r = wave * 32 + (lane >> 1), h = lane & 1;
   const uint8_t* wp = ring + (step % LmLayout::kStages) * LmLayout::kStage + LmLayout::kXStage + r * 32;
-  const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(wp);
-  const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(wp + 16);
+  const u32x4_t d = *reinterpret_cast<const u32x4_t*>(wp + 16 * h);
   const uint32_t sc = *reinterpret_cast<const uint32_t*>(
       ring + LmLayout::kWin + ((step / 4) & 1) * LmLayout::kWinBytes + r * 16 + 4 * (step % 4));
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    w.d[c] = lo[c];
-    w.d[4 + c] = hi[c];
-  }
-  w.sv[0] = decode_e4m3<0>(sc);
-  w.sv[1] = decode_e4m3<1>(sc);
-  w.sv[2] = decode_e4m3<2>(sc);
-  w.sv[3] = decode_e4m3<3>(sc);
+  for (int c = 0; c < 4; ++c) w.d[c] = d[c];
+  w.sc = sc >> (16 * h);
 }
 
-// Write a dequantized row (8 chunks of 8 BF16) into the BF16 weight tile.
-__device__ __forceinline__ void lm_write_wbf(uint8_t* ring, const bf16x8_t (&v)[8], int wave, int lane) {
-  const int r = wave * 64 + lane;
+// Write a lane's 4 dequantized chunks (8 BF16 each) into the BF16 weight tile.
+__device__ __forceinline__ void lm_write_wbf(uint8_t* ring, const bf16x8_t (&v)[4], int wave, int lane) {
+  const int r = wave * 32 + (lane >> 1), h = lane & 1;
   uint8_t* wb = ring + LmLayout::kWbf;
 #pragma unroll
-  for (int c = 0; c < 8; ++c) *reinterpret_cast<bf16x8_t*>(wb + lm_swz(r, c)) = v[c];
+  for (int c = 0; c < 4; ++c) *reinterpret_cast<bf16x8_t*>(wb + lm_swz(r, 4 * h + c)) = v[c];
 }
 
-// 64 MFMAs of one step for the wave's 128 x 128 quadrant: 4 K sub-steps of
-// 16, each reading 4 A and 4 B fragments (lane l: row / column l % 32,
-// K 8 (l / 32) .. +7 of the sub-step).  The next step's weight row is
-// dequantized into registers between the MFMAs (chunk 2 ks + half after
-// each group of 8), where its VALU work overlaps the matrix pipeline.
-__device__ __forceinline__ void lm_frags(bf16x8_t (&a)[4], bf16x8_t (&b)[4], const uint8_t* xs,
+// 32 MFMAs of one step for the wave's 128 x 64 block: 4 K sub-steps of 16,
+// each reading 4 A and 2 B fragments (lane l: row / column l % 32, K 8 (l /
+// 32) .. +7 of the sub-step).  The lane's share of the next step's weights
+// is dequantized between the MFMAs (one chunk per sub-step), where its VALU
+// work overlaps the matrix pipeline.
+__device__ __forceinline__ void lm_frags(bf16x8_t (&a)[4], bf16x8_t (&b)[2], const uint8_t* xs,
                                          const uint8_t* wb, int ks, int wm, int wn, int lane) {
   const int r32 = lane & 31, h = lane >> 5;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     a[i] = *reinterpret_cast<const bf16x8_t*>(xs + lm_swz(wm * 128 + i * 32 + r32, 2 * ks + h));
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    b[j] = *reinterpret_cast<const bf16x8_t*>(wb + lm_swz(wn * 128 + j * 32 + r32, 2 * ks + h));
+  for (int j = 0; j < 2; ++j)
+    b[j] = *reinterpret_cast<const bf16x8_t*>(wb + lm_swz(wn * 64 + j * 32 + r32, 2 * ks + h));
 }
 
-__device__ __forceinline__ void lm_mma(f32x16_t (&acc)[4][4], const uint8_t* xs, const uint8_t* wb,
+__device__ __forceinline__ void lm_mma(f32x16_t (&acc)[4][2], const uint8_t* xs, const uint8_t* wb,
                                        int wm, int wn, int lane, bool dq, const LmWp& w,
-                                       bf16x8_t (&v)[8]) {
+                                       bf16x8_t (&v)[4]) {
   // fragments of sub-step ks + 1 are read while sub-step ks is multiplied
-  bf16x8_t a[2][4], b[2][4];
+  bf16x8_t a[2][4], b[2][2];
   lm_frags(a[0], b[0], xs, wb, 0, wm, wn, lane);
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     if (ks + 1 < 4) lm_frags(a[(ks + 1) & 1], b[(ks + 1) & 1], xs, wb, ks + 1, wm, wn, lane);
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 2 * half; i < 2 * half + 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks & 1][i], b[ks & 1][j], acc[i][j],
-                                                              0, 0, 0);
-      if (dq) {
-        const int c = 2 * ks + half;
-        v[c] = dequant8(w.d[c], w.sv[c >> 1]);
-      }
-    }
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks & 1][i], b[ks & 1][j], acc[i][j],
+                                                            0, 0, 0);
+    if (dq) v[ks] = dequant8(w.d[ks], (ks >> 1) ? decode_e4m3<1>(w.sc) : decode_e4m3<0>(w.sc));
   }
 }
 
 // Dense only (offsets == nullptr, one expert): tile t of the grid is
 // (row tile t / n_tiles, column tile t % n_tiles) after an XCD-aware remap.
-__global__ __launch_bounds__(256) void gemm_lm_kernel(GemmParams p) {
+__global__ __launch_bounds__(LmLayout::kWaves * 64) void gemm_lm_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t ring[LmLayout::kTotal];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;  // 128-row half, 64-column quarter
   const int N = p.n, K = p.k;
   const int m_tiles = (int)((p.rows + kLmBM - 1) / kLmBM);
   const int total = m_tiles * p.n_tiles;
@@ -913,11 +907,11 @@ __global__ __launch_bounds__(256) void gemm_lm_kernel(GemmParams p) {
     const u32x4_t rs = rsrc_words(p.s + (int64_t)n0 * (K / 16),
                                   (uint32_t)(min(N - n0, kLmBN)) * (uint32_t)(K / 16));
 
-    f32x16_t acc[4][4];
+    f32x16_t acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
@@ -929,7 +923,7 @@ __global__ __launch_bounds__(256) void gemm_lm_kernel(GemmParams p) {
     // the BF16 tile of step s) those registers become the BF16 tile of
     // step s + 1.
     LmWp wq;
-    bf16x8_t v[8];
+    bf16x8_t v[4];
     lm_issue(ring0, 0, rx, rw, rs, off, wave);
     if (nsteps > 1) lm_issue(ring0, 1, rx, rw, rs, off, wave);
     // step 0 complete: only step 1's loads may remain
@@ -937,7 +931,8 @@ __global__ __launch_bounds__(256) void gemm_lm_kernel(GemmParams p) {
     __syncthreads();
     lm_read_wp(wq, ring, 0, wave, lane);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) v[c] = dequant8(wq.d[c], wq.sv[c >> 1]);
+    for (int c = 0; c < 4; ++c)
+      v[c] = dequant8(wq.d[c], (c >> 1) ? decode_e4m3<1>(wq.sc) : decode_e4m3<0>(wq.sc));
     lm_write_wbf(ring, v, wave, lane);
 
     for (int s = 0; s < nsteps; ++s) {
@@ -963,8 +958,8 @@ __global__ __launch_bounds__(256) void gemm_lm_kernel(GemmParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = n0 + wn * 128 + j * 32 + r32;
+      for (int j = 0; j < 2; ++j) {
+        const int col = n0 + wn * 64 + j * 32 + r32;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int row = row0 + wm * 128 + i * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
@@ -1215,7 +1210,7 @@ static int occupancy_for(const GemmPlan& pl) {
           : pl.bm == 32 ? occupancy_of(gemm_reg_kernel<32>, kRegThreads, dyn)
                         : occupancy_of(gemm_reg_kernel<64>, kRegThreads, dyn);
     } else if (pl.kind == 3) {
-      c = occupancy_of(gemm_lm_kernel, 256, dyn);
+      c = occupancy_of(gemm_lm_kernel, LmLayout::kWaves * 64, dyn);
     } else if (pl.kind == 1) {
       c = pl.bm == 16 ? occupancy_of(gemm_kp_kernel<16, 5, 4, 128>, 256, dyn)
                       : occupancy_of(gemm_kp_kernel<32, 4, 4, 128>, 256, dyn);
@@ -1288,7 +1283,7 @@ hipError_t launch_gemm(const GemmPlan& pl, const GemmParams& p, hipStream_t stre
 #define NVFP4_KP(BM, NS, KW, BN) \
   hipLaunchKernelGGL((gemm_kp_kernel<BM, NS, KW, BN>), grid, dim3(KW * 64), pl.dyn_lds, stream, p)
   if (pl.kind == 3) {
-    hipLaunchKernelGGL(gemm_lm_kernel, grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(gemm_lm_kernel, grid, dim3(LmLayout::kWaves * 64), 0, stream, p);
   } else if (pl.kind == 1) {
     if (pl.bm == 16) NVFP4_KP(16, 5, 4, 128);
     else NVFP4_KP(32, 4, 4, 128);

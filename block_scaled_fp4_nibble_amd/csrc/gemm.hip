@@ -140,6 +140,26 @@ struct Sched {
   int flag;
 };
 
+// Widest output for which a row tile's bytes (at most 64 rows of FP32)
+// stay inside one 32-bit buffer range.
+constexpr int kFixedStoreMaxN = (1 << 23);
+
+// A uniform 32-bit load through the scalar cache (the data are inputs this
+// kernel never writes, so the load needs no ordering against its stores);
+// it waits on the LDS/scalar counter only, so loads in flight on the vector
+// memory counter are not waited for.
+__device__ __forceinline__ uint32_t sload_u32(const void* base, uint32_t byte_off) {
+  // the address is uniform; say so, so that it stays in SGPRs
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint64_t ua = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a) |
+                      ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32);
+  uint32_t v;
+  asm volatile("s_load_dword %0, %1, %2\n\ts_waitcnt lgkmcnt(0)"
+               : "=s"(v)
+               : "s"(ua), "s"(__builtin_amdgcn_readfirstlane(byte_off)));
+  return v;
+}
+
 __device__ __forceinline__ int seg_begin(const GemmParams& p, int e) {
   return p.offsets ? p.offsets[e] : (e == 0 ? 0 : (int)p.rows);
 }
@@ -147,7 +167,7 @@ __device__ __forceinline__ int seg_begin(const GemmParams& p, int e) {
 // Fills `sc`; returns the total unit count, or -1 (after flagging the status
 // word) when the offsets are malformed.
 template <int THREADS, int BM>
-__device__ int build_schedule(Sched& sc, const GemmParams& p) {
+__device__ __forceinline__ int build_schedule(Sched& sc, const GemmParams& p) {
   const int tid = threadIdx.x;
   const int E = p.num_experts;
   constexpr int PER = (kMaxExperts + THREADS - 1) / THREADS;  // experts per thread
@@ -212,8 +232,10 @@ __device__ __forceinline__ Unit decode_unit(const Sched& sc, const GemmParams& p
   }
   Unit u;
   u.e = __builtin_amdgcn_readfirstlane(lo);
-  const int seg0 = __builtin_amdgcn_readfirstlane(seg_begin(p, u.e));
-  const int seg1 = __builtin_amdgcn_readfirstlane(seg_begin(p, u.e + 1));
+  // segment bounds through the scalar cache: a vector load here would make
+  // the compiler wait for every load in flight, prefetched stages included
+  const int seg0 = p.offsets ? (int)sload_u32(p.offsets, 4u * (uint32_t)u.e) : 0;
+  const int seg1 = p.offsets ? (int)sload_u32(p.offsets, 4u * (uint32_t)(u.e + 1)) : (int)p.rows;
   const int mtiles = (seg1 - seg0 + BM - 1) / BM;
   const int local = unit - sched_units[u.e];
   const int mt = local % mtiles;
@@ -302,6 +324,34 @@ __device__ __forceinline__ bool finish_tile(f32x4_t (&acc)[NF][NW], const GemmPa
     if (tid == 0) __hip_atomic_store(&p.counters[u.tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   const int q = lane >> 4, r16 = lane & 15;
+  if (p.n <= kFixedStoreMaxN) {
+    // One buffer store per accumulator element, always issued (elements
+    // outside the tile get an offset past the resource and are dropped), so
+    // this epilogue issues exactly 4 NF NW vector memory instructions.
+    const int esz = p.out_f32 ? 4 : 2;
+    const __amdgpu_buffer_rsrc_t ry =
+        make_rsrc(static_cast<const char*>(p.y) + (int64_t)u.row0 * p.n * esz,
+                  (uint32_t)((u.row_end - u.row0) * p.n * esz));
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int j = 0; j < NW; ++j) {
+        const int col = u.nt * BN + wave * (NW * 16) + j * 16 + r16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = u.row0 + f * 16 + 4 * q + r;
+          const uint32_t off = (row < u.row_end && col < p.n)
+                                   ? (uint32_t)(((row - u.row0) * p.n + col) * esz)
+                                   : kOffNone;
+          const float v = gv * acc[f][j][r];
+          if (p.out_f32)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), ry, off, 0, 0);
+          else
+            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)float_to_bf16_rne(v), ry, off, 0, 0);
+        }
+      }
+    return true;
+  }
 #pragma unroll
   for (int f = 0; f < NF; ++f)
 #pragma unroll
@@ -391,24 +441,37 @@ struct KpLayout {
   static constexpr int kXInstr = BM / 4;            // 1 KB (4-row) activation loads
   static constexpr int kXPerWave = kXInstr >= KW ? kXInstr / KW : 1;
   static constexpr int kLoadsPerStage = kWPerWave + kXPerWave;
-  // A scale window covers kWinStages stages (8 bytes per row each) and goes
-  // out just before its first stage, into the buffer of the window two back;
-  // that buffer is free once every wave has read that window's last stage,
-  // which holds when NSLOT <= kWinStages + 1.
+  // A scale window covers kWinStages stages (8 bytes per row each) of one
+  // unit and goes out just before its first stage.  Windows take three
+  // buffers in stream order; a buffer is refilled three windows later, after
+  // every wave has read the window it held (NSLOT <= kWinStages + 1 keeps
+  // that true even across units whose last window is short).
   static constexpr int kWinStages = NSLOT <= 3 ? 2 : 4;
+  static constexpr int kWinBufs = 3;
   static constexpr int kWinRow = 8 * kWinStages;    // window bytes per weight row
   static constexpr int kWinBytes = BN * kWinRow;
   static constexpr int kSInstr = kWinBytes / 1024;  // 1 KB scale window loads
   static constexpr int kSWin = NSLOT * kStage;
-  static constexpr int kTotal = kSWin + 2 * kWinBytes;
+  static constexpr int kTotal = kSWin + kWinBufs * kWinBytes;
   static constexpr int kSPerWave = kSInstr >= KW ? kSInstr / KW : 1;
+  // K-half exchange at the end of a unit: 1 KB chunks, kRedSlots ring slots
+  static constexpr int kChunksPerStage = kStage / 1024;
+  static constexpr int kRedChunks = KW * (BM / 16) * (kNJ / 2);
+  static constexpr int kRedSlots = (kRedChunks + kChunksPerStage - 1) / kChunksPerStage;
+  // stages of the next unit issued during a unit's last iterations (the
+  // other ring slots hold the exchange)
+  static constexpr int kPrefetch = NSLOT - kRedSlots;
+  // vector memory instructions of a unit's epilogue (one store per output
+  // element a wave holds after the exchange)
+  static constexpr int kEpiStores = 4 * (BM / 16) * (kNJ / 2);
   static_assert(kWPerWave >= 1 && kSInstr >= 1 && (kSInstr < KW || kSInstr % KW == 0),
                 "load split");
   static_assert(NSLOT <= kWinStages + 1, "window buffers are reused in time");
   static_assert(kNJ % 2 == 0, "column tiles split between the K halves");
   static_assert(NSLOT >= 3 && NSLOT <= 5, "windows are issued one window ahead");
   static_assert(kTotal + (int)sizeof(Sched) + kSchedLdsMax <= 160 * 1024, "LDS budget");
-  static_assert(kTotal >= KW * (BM / 16) * (kNJ / 2) * 1024, "reduction buffer fits the ring");
+  static_assert(kStage % 1024 == 0 && kRedSlots < NSLOT, "exchange fits the ring");
+  static_assert(kPrefetch >= 1 && kPrefetch <= kWinStages, "prefetch within window 0");
 };
 
 template <int BM, int KW, int BN>
@@ -419,8 +482,10 @@ struct KpOffsets {
   uint32_t s[2];
 };
 
+// Per-lane offsets of a wave's loads, relative to the unit's first weight
+// row and first activation row (the same for every unit).
 template <int BM, int NSLOT, int KW, int BN>
-__device__ __forceinline__ KpOffsets<BM, KW, BN> kp_offsets(int n0, int K, int wave, int lane) {
+__device__ __forceinline__ KpOffsets<BM, KW, BN> kp_offsets(int K, int wave, int lane) {
   using L = KpLayout<BM, NSLOT, KW, BN>;
   KpOffsets<BM, KW, BN> o;
   // weights: load t covers rows 16t..16t+15 (64 B each); slot s of row R
@@ -429,7 +494,7 @@ __device__ __forceinline__ KpOffsets<BM, KW, BN> kp_offsets(int n0, int K, int w
   for (int tt = 0; tt < L::kWPerWave; ++tt) {
     const int R = (wave * L::kWPerWave + tt) * 16 + (lane >> 2);
     const int g = (lane & 3) ^ ((R >> 2) & 3);
-    o.w[tt] = (uint32_t)(n0 + R) * (uint32_t)(K / 2) + (uint32_t)(16 * g);
+    o.w[tt] = (uint32_t)R * (uint32_t)(K / 2) + (uint32_t)(16 * g);
   }
   // activations: load t covers rows 4t..4t+3 (256 B each); slot s of row r
   // receives chunk s ^ (r & 15).  With fewer loads than waves, waves repeat
@@ -450,9 +515,31 @@ __device__ __forceinline__ KpOffsets<BM, KW, BN> kp_offsets(int n0, int K, int w
     constexpr int LPR = L::kWinRow / 16;  // lanes per row
     const int t = L::kSInstr >= KW ? wave * L::kSPerWave + tt : wave % L::kSInstr;
     const int R = t * (64 / LPR) + lane / LPR;
-    o.s[tt] = (uint32_t)(n0 + R) * (uint32_t)(K / 16) + (uint32_t)(16 * (lane % LPR));
+    o.s[tt] = (uint32_t)R * (uint32_t)(K / 16) + (uint32_t)(16 * (lane % LPR));
   }
   return o;
+}
+
+// A unit's load sources: buffer descriptors based at its expert's first
+// weight row of the column tile and at its first activation row, and its K
+// range in 128-deep stages.
+struct KpU {
+  u32x4_t rw, rs, rx;
+  int k_beg, k_end, nch;
+};
+
+template <int BN>
+__device__ __forceinline__ KpU kp_unit(const GemmParams& p, const Unit& u) {
+  const int N = p.n, K = p.k;
+  const int n0 = u.nt * BN;
+  KpU s;
+  s.rw = rsrc_words(p.w + ((int64_t)u.e * N + n0) * (K / 2), (uint32_t)(N - n0) * (uint32_t)(K / 2));
+  s.rs = rsrc_words(p.s + ((int64_t)u.e * N + n0) * (K / 16), (uint32_t)(N - n0) * (uint32_t)(K / 16));
+  s.rx = rsrc_words(p.x + (int64_t)u.row0 * K, (uint32_t)(u.row_end - u.row0) * (uint32_t)(K * 2));
+  s.k_beg = u.k_beg;
+  s.k_end = u.k_end;
+  s.nch = (u.k_end - u.k_beg + kRingKC - 1) / kRingKC;
+  return s;
 }
 
 // TAIL: the stage may reach past the end of the unit's K range (only its
@@ -549,56 +636,70 @@ __device__ __forceinline__ void kp_mma(f32x4_t (&acc)[BM / 16][NJ], const KpRegs
 // The K loop of one unit, for tiles whose rows fill NFE of the BM / 16 row
 // fragments (fragments past NFE are pure padding and are skipped).
 //
-// Per unit (per wave, in issue order): stages 0 .. NSLOT-1, each preceded by
-// the scale window that starts at it (every WS-th stage).  Iteration c waits
-// until stage c + 1 has landed and passes the barrier: every wave has then
-// read stage c into registers (in iteration c - 1, or before the loop when
-// c = 0), so stage c's slot takes stage c + NSLOT.  It then reads stage c + 1
-// into registers and multiplies out stage c.
+// The workgroup's units form one stream of stages: stage c of a unit lives
+// in ring slot (sb0 + c) % NSLOT and window i of a unit in buffer
+// (wb0 + i) % 3.  Per unit (per wave, in issue order): stages 0 .. NSLOT-1,
+// each preceded by the scale window that starts at it (every WS-th stage).
+// The first `pf` of them may already be in flight, issued during the
+// previous unit's last iterations and followed there by `ex` epilogue
+// stores.  Iteration c waits until stage c + 1 has landed and passes the
+// barrier: every wave has then read stage c into registers (in iteration
+// c - 1, or before the loop when c = 0), so stage c's slot takes stage
+// c + NSLOT -- or, in the unit's last iterations, one of the next unit's
+// first `pn` stages.  It then reads stage c + 1 into registers and
+// multiplies out stage c.
 //
-// While the stage issued is neither past the end nor the unit's last one,
-// the iterations run in blocks of WS whose waits, window issues and K checks
-// are compile-time constants; the remaining iterations take the general path.
+// While the stage issued lies inside the unit's K range (the last stage only
+// when it is full), the iterations run in blocks of WS whose waits, window
+// issues and K checks are compile-time constants; the remaining iterations
+// take the general path.
 template <int BM, int NSLOT, int KW, int BN, int NFE>
 __device__ __forceinline__ void kp_kloop(f32x4_t (&acc)[BM / 16][2 * BN / KW / 16],
-                                         uint8_t* ring, const Unit& u, u32x4_t rw, u32x4_t rs,
-                                         u32x4_t rx, const KpOffsets<BM, KW, BN>& off, int kp,
-                                         int ch, int wave, int lane) {
+                                         uint8_t* ring, const KpU& cu, int sb0, int wb0, int pf,
+                                         bool ex, const KpU& nx, int pn,
+                                         const KpOffsets<BM, KW, BN>& off, int kp, int ch,
+                                         int wave, int lane) {
   using L = KpLayout<BM, NSLOT, KW, BN>;
   constexpr int NJ = L::kNJ;
   constexpr int D = NSLOT;  // stages in flight after an iteration's issue
   constexpr int WS = L::kWinStages;
   constexpr int LS = L::kLoadsPerStage;
   constexpr int SPW = L::kSPerWave;
+  constexpr int E = L::kEpiStores;
   static_assert(WS % 2 == 0, "blocks keep the register double buffer in phase");
   const int q = lane >> 4;
   const uint32_t ring0 = lds_addr(ring);
-  const int nch = (u.k_end - u.k_beg + kRingKC - 1) / kRingKC;
+  const int nch = cu.nch;
+  const int nwin = (nch + WS - 1) / WS;
+  auto slot = [&](int c) { return ((sb0 + c) % NSLOT) * L::kStage; };
+  auto wbuf = [&](int i) { return L::kSWin + ((wb0 + i) % L::kWinBufs) * L::kWinBytes; };
   // K validity of this lane's scale block in stage c
-  auto kvalid = [&](int c) { return u.k_beg + c * kRingKC + 64 * kp + 16 * q < u.k_end; };
+  auto kvalid = [&](int c) { return cu.k_beg + c * kRingKC + 64 * kp + 16 * q < cu.k_end; };
   auto issue_stage = [&](int st) {
     if (st % WS == 0)
-      kp_issue_scales<BM, NSLOT, KW, BN>(ring0 + L::kSWin + ((st / WS) & 1) * L::kWinBytes, rs,
-                                         off, u.k_beg + st * kRingKC, wave);
-    kp_issue<BM, NSLOT, KW, BN>(ring0 + (st % NSLOT) * L::kStage, rw, rx, off,
-                                u.k_beg + st * kRingKC, u.k_end, wave);
+      kp_issue_scales<BM, NSLOT, KW, BN>(ring0 + wbuf(st / WS), cu.rs, off,
+                                         cu.k_beg + st * kRingKC, wave);
+    kp_issue<BM, NSLOT, KW, BN>(ring0 + slot(st), cu.rw, cu.rx, off, cu.k_beg + st * kRingKC,
+                                cu.k_end, wave);
   };
-  // loads this wave issued after those of stage lo, through stage hi
+  // loads this wave issued after those of stage lo, through stage hi, plus
+  // the epilogue stores when stage lo was issued before them
   auto loads_after = [&](int lo, int hi) {
-    int n = 0;
+    int n = (ex && lo < pf) ? E : 0;
 #pragma unroll
     for (int i = 1; i < D; ++i)
       if (lo + i <= hi) n += LS + ((lo + i) % WS == 0 ? SPW : 0);
     return n;
   };
-  for (int st = 0; st < D && st < nch; ++st) issue_stage(st);
+  int nx_ops = 0;  // loads issued for the next unit so far
+  for (int st = pf; st < D && st < nch; ++st) issue_stage(st);
   wait_vmcnt(loads_after(0, min(D, nch) - 1));
   __syncthreads();
   KpRegs<BM, NJ> ra, rb;
-  kp_read<BM, NJ, NFE, BN, WS>(ra, ring, ring + L::kSWin, 0, kvalid(0), kp, ch, lane);
+  kp_read<BM, NJ, NFE, BN, WS>(ra, ring + slot(0), ring + wbuf(0), 0, kvalid(0), kp, ch, lane);
 
   // iteration c = c0 + T of a steady block (c0 % WS == 0): stages c + 1 ..
-  // c + D - 1 are in flight and full, stage c + D is full and not the last
+  // c + D - 1 are in flight and full, stage c + D is full
   auto steady = [&](auto tc, int c0, const KpRegs<BM, NJ>& cur, KpRegs<BM, NJ>& nxt) {
     constexpr int T = decltype(tc)::value;
     constexpr int kAfter = [] {
@@ -607,33 +708,47 @@ __device__ __forceinline__ void kp_kloop(f32x4_t (&acc)[BM / 16][2 * BN / KW / 1
       return n;
     }();
     const int c = c0 + T;
-    wait_vmcnt_c<kAfter>();
+    if (ex && c + 1 < pf) wait_vmcnt_c<kAfter + E>();
+    else wait_vmcnt_c<kAfter>();
     __syncthreads();
     if constexpr ((T + D) % WS == 0)
-      kp_issue_scales<BM, NSLOT, KW, BN>(
-          ring0 + L::kSWin + (((c + D) / WS) & 1) * L::kWinBytes, rs, off,
-          u.k_beg + (c + D) * kRingKC, wave);
-    kp_issue<BM, NSLOT, KW, BN, false>(ring0 + ((c + D) % NSLOT) * L::kStage, rw, rx, off,
-                                       u.k_beg + (c + D) * kRingKC, u.k_end, wave);
-    kp_read<BM, NJ, NFE, BN, WS>(nxt, ring + ((c + 1) % NSLOT) * L::kStage,
-                                 ring + L::kSWin + (((c + 1) / WS) & 1) * L::kWinBytes,
-                                 (T + 1) % WS, true, kp, ch, lane);
+      kp_issue_scales<BM, NSLOT, KW, BN>(ring0 + wbuf((c + D) / WS), cu.rs, off,
+                                         cu.k_beg + (c + D) * kRingKC, wave);
+    kp_issue<BM, NSLOT, KW, BN, false>(ring0 + slot(c + D), cu.rw, cu.rx, off,
+                                       cu.k_beg + (c + D) * kRingKC, cu.k_end, wave);
+    kp_read<BM, NJ, NFE, BN, WS>(nxt, ring + slot(c + 1), ring + wbuf((c + 1) / WS), (T + 1) % WS,
+                                 true, kp, ch, lane);
     kp_mma<BM, NJ, NFE>(acc, cur);
   };
   auto step = [&](int c, const KpRegs<BM, NJ>& cur, KpRegs<BM, NJ>& nxt) {
     if (c + 1 < nch) {
-      // stages c + 1 .. min(c + D - 1, nch - 1) are in flight
-      wait_vmcnt(loads_after(c + 1, min(c + D - 1, nch - 1)));
+      // stages c + 1 .. min(c + D - 1, nch - 1) are in flight, then the
+      // next unit's loads issued so far
+      wait_vmcnt(loads_after(c + 1, min(c + D - 1, nch - 1)) + nx_ops);
       __syncthreads();
-      if (c + D < nch) issue_stage(c + D);
-      kp_read<BM, NJ, NFE, BN, WS>(nxt, ring + ((c + 1) % NSLOT) * L::kStage,
-                                   ring + L::kSWin + (((c + 1) / WS) & 1) * L::kWinBytes,
+      if (c + D < nch) {
+        issue_stage(c + D);
+      } else if (c + D - nch < pn) {
+        // the next unit's stage j goes where this unit's stage c was; its
+        // first window (j = 0) goes first
+        const int j = c + D - nch;
+        if (j == 0) {
+          kp_issue_scales<BM, NSLOT, KW, BN>(ring0 + wbuf(nwin), nx.rs, off, nx.k_beg, wave);
+          nx_ops += SPW;
+        }
+        kp_issue<BM, NSLOT, KW, BN>(ring0 + slot(c + D), nx.rw, nx.rx, off,
+                                    nx.k_beg + j * kRingKC, nx.k_end, wave);
+        nx_ops += LS;
+      }
+      kp_read<BM, NJ, NFE, BN, WS>(nxt, ring + slot(c + 1), ring + wbuf((c + 1) / WS),
                                    (c + 1) % WS, kvalid(c + 1), kp, ch, lane);
     }
     kp_mma<BM, NJ, NFE>(acc, cur);
   };
+  const bool full_last = cu.k_end - cu.k_beg == nch * kRingKC;
+  const int c_lim = nch - WS - D + (full_last ? 1 : 0);
   int c = 0;
-  for (; c + WS + D < nch; c += WS) {
+  for (; c < c_lim; c += WS) {
     steady(std::integral_constant<int, 0>{}, c, ra, rb);
     steady(std::integral_constant<int, 1>{}, c, rb, ra);
     if constexpr (WS == 4) {
@@ -653,27 +768,40 @@ __global__ __launch_bounds__(KW * 64) void gemm_kp_kernel(GemmParams p) {
   constexpr int NF = BM / 16;
   constexpr int NJ = L::kNJ;
   constexpr int NH = NJ / 2;  // column tiles a wave keeps after the K-half exchange
+  constexpr int CPS = L::kChunksPerStage;
   __shared__ __attribute__((aligned(16))) uint8_t ring[L::kTotal];
   __shared__ Sched sc;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int kp = wave & 1, ch = wave >> 1;
   const int total = build_schedule<KW * 64, BM>(sc, p);
-  const int N = p.n, K = p.k;
+  const int G = gridDim.x;
+  // the workgroup's units are round_unit(round, blockIdx.x, G) for rounds
+  // while the unit id is below total (the grid may exceed the unit count of
+  // a grouped product, and the map permutes workgroups within a round)
+  const int first = round_unit(0, blockIdx.x, G);
+  if (total <= 0 || first >= total) return;
+  const KpOffsets<BM, KW, BN> off = kp_offsets<BM, NSLOT, KW, BN>(p.k, wave, lane);
+  // the next unit's first stages are prefetched only when the epilogue's
+  // store count is fixed (no K split, output addressable by buffer stores)
+  const bool can_pf = p.splits == 1 && p.n <= kFixedStoreMaxN;
 
-  for (int round = 0; round * (int)gridDim.x < total; ++round) {
-    const int unit = round_unit(round, blockIdx.x, gridDim.x);
-    if (unit >= total) continue;
-    const Unit u = decode_unit<BM>(sc, p, unit);
-    const int n0 = u.nt * BN;
-    const u32x4_t rw =
-        rsrc_words(p.w + (int64_t)u.e * N * (K / 2), (uint32_t)N * (uint32_t)(K / 2));
-    const u32x4_t rs =
-        rsrc_words(p.s + (int64_t)u.e * N * (K / 16), (uint32_t)N * (uint32_t)(K / 16));
-    const u32x4_t rx =
-        rsrc_words(p.x + (int64_t)u.row0 * K, (uint32_t)(u.row_end - u.row0) * (uint32_t)(K * 2));
-    const KpOffsets<BM, KW, BN> off = kp_offsets<BM, NSLOT, KW, BN>(n0, K, wave, lane);
-    const float gv = p.g[u.e];  // issued now, first used in the epilogue
+  int round = 0;
+  Unit u = decode_unit<BM>(sc, p, first);
+  KpU cu = kp_unit<BN>(p, u);
+  int sb0 = 0, wb0 = 0, pf = 0;
+  bool ex = false;
+  for (;;) {
+    const int nu = round_unit(round + 1, blockIdx.x, G);
+    const bool has_next = nu < total;
+    Unit un = u;
+    KpU nx = cu;
+    if (has_next) {
+      un = decode_unit<BM>(sc, p, nu);
+      nx = kp_unit<BN>(p, un);
+    }
+    const int pn = (has_next && can_pf && cu.nch >= NSLOT) ? min(L::kPrefetch, nx.nch) : 0;
+    const float gv = __uint_as_float(sload_u32(p.g, 4u * (uint32_t)u.e));
     // 16-row fragments holding rows of this tile (the rest is padding)
     const int nf = min(NF, (u.row_end - u.row0 + 15) / 16);
 
@@ -683,8 +811,9 @@ __global__ __launch_bounds__(KW * 64) void gemm_kp_kernel(GemmParams p) {
 #pragma unroll
       for (int j = 0; j < NJ; ++j) acc[f][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-#define NVFP4_KLOOP(NFE) \
-  kp_kloop<BM, NSLOT, KW, BN, NFE>(acc, ring, u, rw, rs, rx, off, kp, ch, wave, lane)
+#define NVFP4_KLOOP(NFE)                                                                         \
+  kp_kloop<BM, NSLOT, KW, BN, NFE>(acc, ring, cu, sb0, wb0, pf, ex, nx, pn, off, kp, ch, wave, \
+                                   lane)
     switch (nf) {
       case 1: NVFP4_KLOOP(1); break;
       case 2: NVFP4_KLOOP(NF >= 2 ? 2 : NF); break;
@@ -694,11 +823,13 @@ __global__ __launch_bounds__(KW * 64) void gemm_kp_kernel(GemmParams p) {
 #undef NVFP4_KLOOP
 
     // Sum the two K halves: wave w keeps column tiles [NH kp, NH kp + NH) of
-    // its NJ and hands the others to wave w ^ 1 through LDS (the ring is idle).
+    // its NJ and hands the others to wave w ^ 1 through 1 KB chunks in the
+    // ring slots not holding the next unit's first stages.
     __syncthreads();
-    f32x4_t* red = reinterpret_cast<f32x4_t*>(ring) + wave * (NF * NH * kWave) + lane;
-    const f32x4_t* peer =
-        reinterpret_cast<const f32x4_t*>(ring) + (wave ^ 1) * (NF * NH * kWave) + lane;
+    auto chunk = [&](int k) {
+      const int sl = (sb0 + cu.nch + pn + k / CPS) % NSLOT;
+      return reinterpret_cast<f32x4_t*>(ring + sl * L::kStage + (k % CPS) * 1024) + lane;
+    };
     f32x4_t out[NF][NH];
     // (the branch is wave-uniform; both sides index the accumulators with
     // constants so they stay in registers)
@@ -706,26 +837,36 @@ __global__ __launch_bounds__(KW * 64) void gemm_kp_kernel(GemmParams p) {
 #pragma unroll
       for (int f = 0; f < NF; ++f)
 #pragma unroll
-        for (int jj = 0; jj < NH; ++jj) red[(f * NH + jj) * kWave] = acc[f][NH + jj];
+        for (int jj = 0; jj < NH; ++jj) *chunk(wave * (NF * NH) + f * NH + jj) = acc[f][NH + jj];
       __syncthreads();
 #pragma unroll
       for (int f = 0; f < NF; ++f)
 #pragma unroll
-        for (int jj = 0; jj < NH; ++jj) out[f][jj] = acc[f][jj] + peer[(f * NH + jj) * kWave];
+        for (int jj = 0; jj < NH; ++jj)
+          out[f][jj] = acc[f][jj] + *chunk((wave ^ 1) * (NF * NH) + f * NH + jj);
     } else {
 #pragma unroll
       for (int f = 0; f < NF; ++f)
 #pragma unroll
-        for (int jj = 0; jj < NH; ++jj) red[(f * NH + jj) * kWave] = acc[f][jj];
+        for (int jj = 0; jj < NH; ++jj) *chunk(wave * (NF * NH) + f * NH + jj) = acc[f][jj];
       __syncthreads();
 #pragma unroll
       for (int f = 0; f < NF; ++f)
 #pragma unroll
-        for (int jj = 0; jj < NH; ++jj) out[f][jj] = peer[(f * NH + jj) * kWave] + acc[f][NH + jj];
+        for (int jj = 0; jj < NH; ++jj)
+          out[f][jj] = *chunk((wave ^ 1) * (NF * NH) + f * NH + jj) + acc[f][NH + jj];
     }
-    __syncthreads();  // the ring is free for the next unit's loads
+    __syncthreads();  // exchange chunks read before the next unit's loads reuse them
     // wave w now owns columns [w CPW/2, (w + 1) CPW/2) of the unit
     finish_tile<NF, NH, KW, BN>(out, p, u, gv, sc);
+    if (!has_next) break;
+    sb0 = (sb0 + cu.nch) % NSLOT;
+    wb0 = (wb0 + (cu.nch + L::kWinStages - 1) / L::kWinStages) % L::kWinBufs;
+    pf = pn;
+    ex = pn > 0;
+    u = un;
+    cu = nx;
+    ++round;
   }
 }
 

@@ -13,15 +13,25 @@
 //   above every finite one, so one integer max both finds amax and detects
 //   non-finite input).  Writes one uint32 per workgroup to the workspace.
 // Pass 2 (encode): every workgroup first folds its tensor's partials
-//   (deterministic, no atomics), derives g, then each thread encodes one
-//   16-value block: 32 bytes in, 8 packed bytes + 1 scale byte out.
+//   (deterministic, no atomics), derives g, then its threads encode 16-value
+//   blocks in a grid-stride loop: 32 bytes in, 8 packed bytes + 1 scale byte
+//   out per block.  The element quotient |w| / d is the correctly rounded
+//   FP32 quotient, as in the definition: for d in [2^-98, 2^100] it is formed
+//   from the correctly rounded reciprocal r = RN(1/d) with one FMA-based
+//   correction (Markstein: q0 = RN(|w| r), e = |w| - q0 d exactly, q =
+//   RN(q0 + e r) = RN(|w| / d) for normal operands); an |w| below 2^-100
+//   then gives a quotient far below the first rounding threshold (0.25), so
+//   its code is 0 either way.  Other blocks use the IEEE division.
 // Both passes stream W with 16-byte loads; W is read twice from HBM.
+#include <algorithm>
+
 #include "device_common.hpp"
 #include "nvfp4_internal.hpp"
 
 namespace nvfp4 {
 
 constexpr int kQThreads = 256;
+constexpr int kQUnroll = 4;  // blocks per thread in flight in the encoder
 
 typedef __attribute__((ext_vector_type(2))) unsigned short u16x2_t;
 
@@ -66,9 +76,17 @@ __global__ __launch_bounds__(kQThreads) void amax_partial_kernel(
   const u32x4_t* src = reinterpret_cast<const u32x4_t*>(w + (int64_t)t * elems);
   const int64_t vecs = elems / 8;
   uint32_t m = 0;
-  for (int64_t i = (int64_t)blockIdx.x * kQThreads + threadIdx.x; i < vecs;
-       i += (int64_t)parts * kQThreads) {
-    m = max_mag_bits(__builtin_nontemporal_load(src + i), m);
+  // kQUnroll loads in flight per thread
+  const int64_t stride = (int64_t)parts * kQThreads;
+  for (int64_t i0 = (int64_t)blockIdx.x * kQThreads + threadIdx.x; i0 < vecs;
+       i0 += stride * kQUnroll) {
+    u32x4_t v[kQUnroll];
+#pragma unroll
+    for (int u = 0; u < kQUnroll; ++u)
+      v[u] = i0 + u * stride < vecs ? __builtin_nontemporal_load(src + i0 + u * stride)
+                                    : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int u = 0; u < kQUnroll; ++u) m = max_mag_bits(v[u], m);
   }
   uint32_t lo = m & 0xFFFFu, hi = m >> 16;
   m = lo > hi ? lo : hi;
@@ -76,7 +94,46 @@ __global__ __launch_bounds__(kQThreads) void amax_partial_kernel(
   if (threadIdx.x == 0) partial[(int64_t)t * parts + blockIdx.x] = m;
 }
 
-// grid: (ceil(blocks16 / kQThreads), batch); one thread per 16-value block.
+// Encode one 16-value block (two 16-byte halves) with global scale g.
+__device__ __forceinline__ void encode_block(u32x4_t v0, u32x4_t v1, float g, uint8_t* packed8,
+                                             uint8_t* scale1) {
+  uint32_t mb = max_mag_bits(v1, max_mag_bits(v0, 0u));
+  uint32_t lo = mb & 0xFFFFu, hi = mb >> 16;
+  const float amax_b = bf16_bits_to_float(lo > hi ? lo : hi);
+
+  uint32_t scode = 0;
+  if (g != 0.0f) {
+    const float t6 = amax_b / kE2M1Max;
+    scode = encode_e4m3(t6 / g);
+  }
+  const float s_dec = decode_e4m3<0>(scode);
+  const float d = s_dec * g;
+  const bool fast = d >= 0x1p-98f && d <= 0x1p100f;
+  const float r = fast ? 1.0f / d : 0.0f;
+
+  uint32_t words[2] = {0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const uint32_t dw = (e < 8) ? v0[e / 2] : v1[(e - 8) / 2];
+    const uint32_t h = (e & 1) ? (dw >> 16) : (dw & 0xFFFFu);
+    const float x = bf16_bits_to_float(h & 0x7FFFu);
+    uint32_t mag = 0;
+    if (fast) {
+      const float q0 = x * r;
+      const float q = __builtin_fmaf(__builtin_fmaf(-q0, d, x), r, q0);
+      mag = encode_e2m1_mag(q);
+    } else if (d != 0.0f) {
+      mag = encode_e2m1_mag(x / d);
+    }
+    const uint32_t code = ((h >> 15) << 3) | mag;
+    words[e / 8] |= code << (4 * (e % 8));
+  }
+  u32x2_t outw = {words[0], words[1]};
+  *reinterpret_cast<u32x2_t*>(packed8) = outw;
+  *scale1 = (uint8_t)scode;
+}
+
+// grid: (encode workgroups, batch); threads stride over the 16-value blocks.
 __global__ __launch_bounds__(kQThreads) void encode_kernel(
     const uint16_t* __restrict__ w, int64_t n, int64_t k, const uint32_t* __restrict__ partial,
     int parts, uint8_t* __restrict__ packed, uint8_t* __restrict__ scales,
@@ -100,38 +157,29 @@ __global__ __launch_bounds__(kQThreads) void encode_kernel(
   if (blockIdx.x == 0 && threadIdx.x == 0) gscale[t] = g;
 
   const int64_t blocks16 = n * (k / 16);
-  const int64_t b = (int64_t)blockIdx.x * kQThreads + threadIdx.x;
-  if (b >= blocks16) return;
   const int64_t elems = n * k;
-  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(w + (int64_t)t * elems + b * 16);
-  u32x4_t v0 = __builtin_nontemporal_load(src);
-  u32x4_t v1 = __builtin_nontemporal_load(src + 1);
-  uint32_t mb = max_mag_bits(v1, max_mag_bits(v0, 0u));
-  uint32_t lo = mb & 0xFFFFu, hi = mb >> 16;
-  const float amax_b = bf16_bits_to_float(lo > hi ? lo : hi);
-
-  uint32_t scode = 0;
-  if (g != 0.0f) {
-    const float t6 = amax_b / kE2M1Max;
-    scode = encode_e4m3(t6 / g);
-  }
-  const float s_dec = decode_e4m3<0>(scode);
-  const float d = s_dec * g;
-
-  uint32_t words[2] = {0u, 0u};
+  // kQUnroll blocks per thread and iteration, loaded before any is encoded,
+  // so each wave keeps that many 32-byte loads in flight
+  const int64_t stride = (int64_t)gridDim.x * kQThreads;
+  for (int64_t b0 = (int64_t)blockIdx.x * kQThreads + threadIdx.x; b0 < blocks16;
+       b0 += stride * kQUnroll) {
+    u32x4_t v[kQUnroll][2];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const uint32_t dw = (e < 8) ? v0[e / 2] : v1[(e - 8) / 2];
-    const uint32_t h = (e & 1) ? (dw >> 16) : (dw & 0xFFFFu);
-    const float x = bf16_bits_to_float(h & 0x7FFFu);
-    uint32_t mag = 0;
-    if (d != 0.0f) mag = encode_e2m1_mag(x / d);
-    const uint32_t code = ((h >> 15) << 3) | mag;
-    words[e / 8] |= code << (4 * (e % 8));
+    for (int i = 0; i < kQUnroll; ++i) {
+      const int64_t b = b0 + i * stride;
+      if (b < blocks16) {
+        const u32x4_t* src = reinterpret_cast<const u32x4_t*>(w + (int64_t)t * elems + b * 16);
+        v[i][0] = __builtin_nontemporal_load(src);
+        v[i][1] = __builtin_nontemporal_load(src + 1);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kQUnroll; ++i) {
+      const int64_t b = b0 + i * stride;
+      if (b < blocks16) encode_block(v[i][0], v[i][1], g, packed + (int64_t)t * (elems / 2) + b * 8,
+                                     scales + (int64_t)t * (elems / 16) + b);
+    }
   }
-  u32x2_t outw = {words[0], words[1]};
-  *reinterpret_cast<u32x2_t*>(packed + (int64_t)t * (elems / 2) + b * 8) = outw;
-  scales[(int64_t)t * (elems / 16) + b] = (uint8_t)scode;
 }
 
 int quantize_parts(int64_t n, int64_t k, int cu_count) {
@@ -153,8 +201,12 @@ hipError_t launch_quantize(const uint16_t* w, int64_t batch, int64_t n, int64_t 
                      parts);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  // encode workgroups: enough to cover the CUs several times over, each
+  // striding over many blocks so the partials are folded few times
   const int64_t blocks16 = n * (k / 16);
-  dim3 g2((unsigned)((blocks16 + kQThreads - 1) / kQThreads), (unsigned)batch);
+  const int64_t wgs =
+      std::min<int64_t>((blocks16 + kQThreads * kQUnroll - 1) / (kQThreads * kQUnroll), 8 * 256);
+  dim3 g2((unsigned)wgs, (unsigned)batch);
   hipLaunchKernelGGL(encode_kernel, g2, dim3(kQThreads), 0, stream, w, n, k, partial, parts,
                      packed, scales, gscale, d_status);
   return hipGetLastError();

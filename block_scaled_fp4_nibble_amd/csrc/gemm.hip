@@ -894,10 +894,13 @@ struct LmLayout {
   static constexpr int kWaves = 8;
   static constexpr int kXStage = kLmBM * kLmBK * 2;          // 32 KB
   static constexpr int kWpStage = kLmBN * kLmBK / 2;         // 8 KB
-  static constexpr int kStage = kXStage + kWpStage;
-  static constexpr int kStages = 3;
-  static constexpr int kWbf = kStages * kStage;              // BF16 weight tile, 32 KB
-  static constexpr int kWin = kWbf + kLmBN * kLmBK * 2;      // 2 scale windows of 4 KB
+  static constexpr int kWbfBytes = kLmBN * kLmBK * 2;        // 32 KB
+  // two activation slots, two packed-weight slots, two BF16 weight tiles,
+  // two scale windows
+  static constexpr int kX = 0;
+  static constexpr int kWp = 2 * kXStage;
+  static constexpr int kWbf = kWp + 2 * kWpStage;
+  static constexpr int kWin = kWbf + 2 * kWbfBytes;
   static constexpr int kWinBytes = kLmBN * 16;
   static constexpr int kTotal = kWin + 2 * kWinBytes;
   static constexpr int kXLoads = kXStage / 1024 / kWaves;    // per wave per step: 4
@@ -939,18 +942,24 @@ __device__ __forceinline__ LmOffsets lm_offsets(int K, int wave, int lane) {
   return o;
 }
 
-__device__ __forceinline__ void lm_issue(uint32_t ring0, int step, u32x4_t rx, u32x4_t rw,
-                                         u32x4_t rs, const LmOffsets& o, int wave) {
-  // order: scale window (with the first step it covers), packed weights,
-  // activations -- the weights of a step are needed one step earlier
+// The packed weights of a step (and, with the first step it covers, a scale
+// window) into weight slot step % 2.
+__device__ __forceinline__ void lm_issue_w(uint32_t ring0, int step, u32x4_t rw, u32x4_t rs,
+                                           const LmOffsets& o, int wave) {
   if (step % 4 == 0 && wave < LmLayout::kWinLoads)
     lds_dma16(ring0 + LmLayout::kWin + ((step / 4) & 1) * LmLayout::kWinBytes + wave * 1024, o.s,
               (uint32_t)(step * kLmBK / 16), rs);
-  const uint32_t st = ring0 + (step % LmLayout::kStages) * LmLayout::kStage;
+  const uint32_t st = ring0 + LmLayout::kWp + (step & 1) * LmLayout::kWpStage;
 #pragma unroll
   for (int tt = 0; tt < LmLayout::kWpLoads; ++tt)
-    lds_dma16(st + LmLayout::kXStage + (wave * LmLayout::kWpLoads + tt) * 1024, o.wp[tt],
-              (uint32_t)(step * kLmBK / 2), rw);
+    lds_dma16(st + (wave * LmLayout::kWpLoads + tt) * 1024, o.wp[tt], (uint32_t)(step * kLmBK / 2),
+              rw);
+}
+
+// The activations of a step into activation slot step % 2.
+__device__ __forceinline__ void lm_issue_x(uint32_t ring0, int step, u32x4_t rx,
+                                           const LmOffsets& o, int wave) {
+  const uint32_t st = ring0 + LmLayout::kX + (step & 1) * LmLayout::kXStage;
 #pragma unroll
   for (int tt = 0; tt < LmLayout::kXLoads; ++tt)
     lds_dma16(st + (wave * LmLayout::kXLoads + tt) * 1024, o.x[tt], (uint32_t)(step * kLmBK * 2),
@@ -968,7 +977,7 @@ struct LmWp {
 
 __device__ __forceinline__ void lm_read_wp(LmWp& w, const uint8_t* ring, int step, int wave, int lane) {
   const int r = wave * 32 + (lane >> 1), h = lane & 1;
-  const uint8_t* wp = ring + (step % LmLayout::kStages) * LmLayout::kStage + LmLayout::kXStage + r * 32;
+  const uint8_t* wp = ring + LmLayout::kWp + (step & 1) * LmLayout::kWpStage + r * 32;
   const u32x4_t d = *reinterpret_cast<const u32x4_t*>(wp + 16 * h);
   const uint32_t sc = *reinterpret_cast<const uint32_t*>(
       ring + LmLayout::kWin + ((step / 4) & 1) * LmLayout::kWinBytes + r * 16 + 4 * (step % 4));
@@ -977,10 +986,11 @@ __device__ __forceinline__ void lm_read_wp(LmWp& w, const uint8_t* ring, int ste
   w.sc = sc >> (16 * h);
 }
 
-// Write a lane's 4 dequantized chunks (8 BF16 each) into the BF16 weight tile.
-__device__ __forceinline__ void lm_write_wbf(uint8_t* ring, const bf16x8_t (&v)[4], int wave, int lane) {
+// Write a lane's 4 dequantized chunks (8 BF16 each) into BF16 weight tile `buf`.
+__device__ __forceinline__ void lm_write_wbf(uint8_t* ring, int buf, const bf16x8_t (&v)[4],
+                                             int wave, int lane) {
   const int r = wave * 32 + (lane >> 1), h = lane & 1;
-  uint8_t* wb = ring + LmLayout::kWbf;
+  uint8_t* wb = ring + LmLayout::kWbf + buf * LmLayout::kWbfBytes;
 #pragma unroll
   for (int c = 0; c < 4; ++c) *reinterpret_cast<bf16x8_t*>(wb + lm_swz(r, 4 * h + c)) = v[c];
 }
@@ -1001,9 +1011,10 @@ __device__ __forceinline__ void lm_frags(bf16x8_t (&a)[4], bf16x8_t (&b)[2], con
     b[j] = *reinterpret_cast<const bf16x8_t*>(wb + lm_swz(wn * 64 + j * 32 + r32, 2 * ks + h));
 }
 
+template <class Hook>
 __device__ __forceinline__ void lm_mma(f32x16_t (&acc)[4][2], const uint8_t* xs, const uint8_t* wb,
                                        int wm, int wn, int lane, bool dq, const LmWp& w,
-                                       bf16x8_t (&v)[4]) {
+                                       bf16x8_t (&v)[4], Hook hook) {
   // fragments of sub-step ks + 1 are read while sub-step ks is multiplied
   bf16x8_t a[2][4], b[2][2];
   lm_frags(a[0], b[0], xs, wb, 0, wm, wn, lane);
@@ -1017,6 +1028,7 @@ __device__ __forceinline__ void lm_mma(f32x16_t (&acc)[4][2], const uint8_t* xs,
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks & 1][i], b[ks & 1][j], acc[i][j],
                                                             0, 0, 0);
     if (dq) v[ks] = dequant8(w.d[ks], (ks >> 1) ? decode_e4m3<1>(w.sc) : decode_e4m3<0>(w.sc));
+    hook(ks);
   }
 }
 
@@ -1033,7 +1045,6 @@ __global__ __launch_bounds__(LmLayout::kWaves * 64) void gemm_lm_kernel(GemmPara
   const uint32_t ring0 = lds_addr(ring);
   const LmOffsets off = lm_offsets(K, wave, lane);
   const int nsteps = K / kLmBK;
-  constexpr int LS = LmLayout::kLoadsPerStage;
   const float gv = p.g[0];
 
   for (int round = 0; round * (int)gridDim.x < total; ++round) {
@@ -1056,40 +1067,42 @@ __global__ __launch_bounds__(LmLayout::kWaves * 64) void gemm_lm_kernel(GemmPara
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-    // Pipeline per iteration s (in issue order): wait until step s + 1's
-    // packed weights have landed (only its activations may still be in
-    // flight), barrier, issue step s + 2 into the slot step s - 1 used, then
-    // run step s's MFMAs from LDS with step s + 1's weights dequantized into
-    // registers between them; after a second barrier (every wave has read
-    // the BF16 tile of step s) those registers become the BF16 tile of
-    // step s + 1.
+    // Pipeline per iteration s: wait for everything issued (the activations
+    // of step s and the packed weights of step s + 1, issued last, in
+    // iteration s - 1), barrier, issue the packed weights of step s + 2 and
+    // the activations of step s + 1 into the slots step s - 1 and step s - 2
+    // used, then run step s's MFMAs from BF16 tile s % 2 with step s + 1's
+    // weights dequantized between them and written into BF16 tile
+    // (s + 1) % 2, which step s - 1's MFMAs were done with at the barrier.
     LmWp wq;
     bf16x8_t v[4];
-    lm_issue(ring0, 0, rx, rw, rs, off, wave);
-    if (nsteps > 1) lm_issue(ring0, 1, rx, rw, rs, off, wave);
-    // step 0 complete: only step 1's loads may remain
-    wait_vmcnt(nsteps > 1 ? LS : 0);
+    lm_issue_w(ring0, 0, rw, rs, off, wave);
+    lm_issue_x(ring0, 0, rx, off, wave);
+    if (nsteps > 1) lm_issue_w(ring0, 1, rw, rs, off, wave);
+    wait_vmcnt_c<0>();
     __syncthreads();
     lm_read_wp(wq, ring, 0, wave, lane);
 #pragma unroll
     for (int c = 0; c < 4; ++c)
       v[c] = dequant8(wq.d[c], (c >> 1) ? decode_e4m3<1>(wq.sc) : decode_e4m3<0>(wq.sc));
-    lm_write_wbf(ring, v, wave, lane);
+    lm_write_wbf(ring, 0, v, wave, lane);
 
     for (int s = 0; s < nsteps; ++s) {
       const bool more = s + 1 < nsteps;
-      // the packed weights of step s + 1 precede its activations in issue
-      // order; the activations (LX loads) may still be in flight
-      wait_vmcnt(more ? LmLayout::kXLoads : 0);
+      wait_vmcnt_c<0>();
       __syncthreads();
-      if (s + 2 < nsteps) lm_issue(ring0, s + 2, rx, rw, rs, off, wave);
       if (more) lm_read_wp(wq, ring, s + 1, wave, lane);
-      lm_mma(acc, ring + (s % LmLayout::kStages) * LmLayout::kStage, ring + LmLayout::kWbf, wm, wn,
-             lane, more, wq, v);
-      if (more) {
-        __syncthreads();
-        lm_write_wbf(ring, v, wave, lane);
-      }
+      // the next steps' loads go out between the MFMA sub-steps, so the
+      // load path works while the matrix pipe does (issued all at once after
+      // the barrier they held every wave for hundreds of cycles)
+      auto issue = [&](int ks) {
+        if (ks == 0 && s + 2 < nsteps) lm_issue_w(ring0, s + 2, rw, rs, off, wave);
+        if (ks == 1 && more) lm_issue_x(ring0, s + 1, rx, off, wave);
+      };
+      lm_mma(acc, ring + LmLayout::kX + (s & 1) * LmLayout::kXStage,
+             ring + LmLayout::kWbf + (s & 1) * LmLayout::kWbfBytes, wm, wn, lane, more, wq, v,
+             issue);
+      if (more) lm_write_wbf(ring, (s + 1) & 1, v, wave, lane);
     }
     __syncthreads();  // all fragment reads done before the next tile's loads
 

@@ -986,13 +986,20 @@ __device__ __forceinline__ void lm_read_wp(LmWp& w, const uint8_t* ring, int ste
   w.sc = sc >> (16 * h);
 }
 
-// Write a lane's 4 dequantized chunks (8 BF16 each) into BF16 weight tile `buf`.
-__device__ __forceinline__ void lm_write_wbf(uint8_t* ring, int buf, const bf16x8_t (&v)[4],
-                                             int wave, int lane) {
+// Write chunk c (8 BF16) of a lane's dequantized weights into BF16 weight
+// tile `buf`.
+__device__ __forceinline__ void lm_write_wbf1(uint8_t* ring, int buf, const bf16x8_t& v, int c,
+                                              int wave, int lane) {
   const int r = wave * 32 + (lane >> 1), h = lane & 1;
   uint8_t* wb = ring + LmLayout::kWbf + buf * LmLayout::kWbfBytes;
+  *reinterpret_cast<bf16x8_t*>(wb + lm_swz(r, 4 * h + c)) = v;
+}
+
+// Write a lane's 4 dequantized chunks into BF16 weight tile `buf`.
+__device__ __forceinline__ void lm_write_wbf(uint8_t* ring, int buf, const bf16x8_t (&v)[4],
+                                             int wave, int lane) {
 #pragma unroll
-  for (int c = 0; c < 4; ++c) *reinterpret_cast<bf16x8_t*>(wb + lm_swz(r, 4 * h + c)) = v[c];
+  for (int c = 0; c < 4; ++c) lm_write_wbf1(ring, buf, v[c], c, wave, lane);
 }
 
 // 32 MFMAs of one step for the wave's 128 x 64 block: 4 K sub-steps of 16,
@@ -1094,15 +1101,18 @@ __global__ __launch_bounds__(LmLayout::kWaves * 64) void gemm_lm_kernel(GemmPara
       if (more) lm_read_wp(wq, ring, s + 1, wave, lane);
       // the next steps' loads go out between the MFMA sub-steps, so the
       // load path works while the matrix pipe does (issued all at once after
-      // the barrier they held every wave for hundreds of cycles)
+      // the barrier they held every wave for hundreds of cycles); so does
+      // each chunk of the next step's BF16 weight tile as soon as it is
+      // dequantized (that buffer's readers, step s - 1, all passed the
+      // barrier above)
       auto issue = [&](int ks) {
         if (ks == 0 && s + 2 < nsteps) lm_issue_w(ring0, s + 2, rw, rs, off, wave);
         if (ks == 1 && more) lm_issue_x(ring0, s + 1, rx, off, wave);
+        if (more) lm_write_wbf1(ring, (s + 1) & 1, v[ks], ks, wave, lane);
       };
       lm_mma(acc, ring + LmLayout::kX + (s & 1) * LmLayout::kXStage,
              ring + LmLayout::kWbf + (s & 1) * LmLayout::kWbfBytes, wm, wn, lane, more, wq, v,
              issue);
-      if (more) lm_write_wbf(ring, (s + 1) & 1, v, wave, lane);
     }
     __syncthreads();  // all fragment reads done before the next tile's loads
 

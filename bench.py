@@ -216,24 +216,28 @@ def extras():
     import block_scaled_fp4_nibble_amd as nv
 
     out = {}
-    # dense decode: N=4096, K=7168; 4 weight copies rotated so each launch reads
-    # a copy not touched for 3 launches (3 x 16.5 MB, still inside the 256 MB
-    # Infinity Cache, so this is a warm-cache figure)
+    # dense decode: N=4096, K=7168.  Warm: 4 weight copies rotated, so each
+    # launch reads a copy not touched for 3 launches (3 x 16.5 MB, inside the
+    # 256 MB Infinity Cache).  Cold: 72 copies (1.19 GB), so each launch reads a
+    # copy not touched for more than 1 GB of traffic and comes from HBM.
     n, k = 4096, 7168
     ws = [nv.quantize(randn_bf16((n, k), 0.02, 200 + i)) for i in range(4)]
+    cold = [nv.QuantizedWeight(ws[i % 4].packed.clone(), ws[i % 4].scales.clone(),
+                               ws[i % 4].global_scale.clone()) for i in range(72)]
     for m in (1, 16, 64):
         x = randn_bf16((m, k), 1.0, 300 + m)
         y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
-        it = [0]
+        for tag, pool, iters in (("", ws, 50), ("_cold", cold, 144)):
+            it = [0]
 
-        def f():
-            nv.gemm(x, ws[it[0] % 4], out=y)
-            it[0] += 1
-        ms = time_fn(f, 50, 10)
-        out["dense_decode_m%d" % m] = {"us": ms * 1e3,
-                                       "GBps": dense_bytes(m, n, k) / (ms * 1e-3) / 1e9,
-                                       "TFLOPS": 2 * m * n * k / (ms * 1e-3) / 1e12}
-    del ws
+            def f():
+                nv.gemm(x, pool[it[0] % len(pool)], out=y)
+                it[0] += 1
+            ms = time_fn(f, iters, len(pool))
+            out["dense_decode_m%d%s" % (m, tag)] = {
+                "us": ms * 1e3, "GBps": dense_bytes(m, n, k) / (ms * 1e-3) / 1e9,
+                "TFLOPS": 2 * m * n * k / (ms * 1e-3) / 1e12}
+    del ws, cold
     # 8192^3 dense GEMM and the bulk quantize of its weight
     m = n = k = 8192
     w = randn_bf16((n, k), 0.02, 400)
@@ -359,8 +363,13 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
-    launch_ms = [sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)) /
-                 args.steps for j in range(len(launches))]
+    samples = [[evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]
+               for j in range(len(launches))]
+    launch_ms = [sum(v) / len(v) for v in samples]
+
+    def pct(v, q):
+        v = sorted(v)
+        return v[min(len(v) - 1, int(round(q * (len(v) - 1))))]
 
     # dominant kernel instantiation by total time
     by_bm = {}
@@ -397,9 +406,10 @@ def main():
                           "nonempty_experts": sum(1 for c in L["counts"] if c),
                           "max_rows_per_expert": max(L["counts"]),
                           "us": ms * 1e3,
+                          "us_p10_median_p90": [pct(v, q) * 1e3 for q in (0.1, 0.5, 0.9)],
                           "TFLOPS": L["flops"] / (ms * 1e-3) / 1e12,
                           "GBps": L["bytes"] / (ms * 1e-3) / 1e9}
-                         for L, ms in zip(launches, launch_ms)],
+                         for L, ms, v in zip(launches, launch_ms, samples)],
         },
         "hbm_gbps": step_bytes / (ms_per_step * 1e-3) / 1e9,
         "hbm_frac": step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,

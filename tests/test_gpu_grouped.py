@@ -191,6 +191,25 @@ def test_single_hot_expert_matches_dense():
     check_close(yd, y_ref, d, "dense")
 
 
+@pytest.mark.parametrize("k", [128, 80])
+def test_expert_limit(k):
+    """NVFP4_MAX_EXPERTS experts, most of them empty: the per-expert unit
+    prefix spans several experts per thread, and units decode through the
+    full-width search (k = 128: K-phase kernel; k = 80: fallback kernel)."""
+    nv = require_gpu()
+    E = nv.MAX_EXPERTS
+    rng = np.random.default_rng(91)
+    counts = np.zeros(E, np.int64)
+    hot = rng.choice(E, 150, replace=False)
+    counts[hot] = rng.integers(1, 41, 150)
+    counts[E - 1] = 7  # the last expert is not empty
+    x, off, w = small_case(counts.tolist(), 64, k, seed=11 + k)
+    p, s, g = oracle_weights(w)
+    y_ref, d = oracle.grouped_gemm(x, off, p, s, g)
+    y = run_grouped(nv, x, off, to_qw(nv, p, s, g), torch.float32)
+    check_close(y, y_ref, d, "E=%d k=%d" % (E, k))
+
+
 @pytest.mark.parametrize("bad", ["decreasing", "first_nonzero", "last_wrong"])
 def test_bad_offsets_set_status_and_write_nothing(bad):
     nv = require_gpu()

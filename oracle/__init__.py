@@ -258,3 +258,65 @@ def grouped_gemm_sampled(x_bf16_bits, offsets, packed, scales, g, rows_idx, cols
     if st != OK:
         raise OracleError("grouped_gemm_sampled failed: %d" % st)
     return y, d
+
+
+# ---- gate_up with the SiLU(gate) * up epilogue -------------------------------
+#
+# "The FP4 Frontier", Finding 5 (persistent kernel recommendations) names the
+# fused MoE MLP: the gate_up grouped GEMM followed by SiLU and the down GEMM.
+# The pages define neither SiLU nor the fused weight's row order; the plain
+# readings are SiLU(v) = v / (1 + e^-v) applied to the gate half and
+# multiplied elementwise by the up half.  The fused weight [n = 2 i, k] holds
+# its rows in 32-row groups: 16 gate rows, then the 16 up rows of the same
+# output columns (output column c pairs weight rows 32 (c / 16) + c % 16 and
+# that + 16).
+
+SILU_SLOPE_MAX = 1.1  # bound on |d SiLU / dv| (its maximum is 1.0998 near v = 2.4)
+
+
+def silu(v):
+    """SiLU(v) = v / (1 + exp(-v)) in float64 (-0.0 for v -> -inf)."""
+    v = np.asarray(v, np.float64)
+    with np.errstate(over="ignore"):
+        return v / (1.0 + np.exp(-v))
+
+
+def gate_up_rows(n: int):
+    """Weight rows (gate, up) feeding each of the n / 2 output columns."""
+    if n % 32:
+        raise ValueError("n must be a multiple of 32")
+    c = np.arange(n // 2)
+    gate = (c // 16) * 32 + c % 16
+    return gate, gate + 16
+
+
+def swiglu(y, d):
+    """h = SiLU(y_gate) * y_up and its error scale D_h from the GEMM's
+    (y, D) over the fused columns: a first-order bound on how errors
+    of size e * D in y move h, D_h = 1.1 D_gate |y_up| + |SiLU(y_gate)| D_up."""
+    y = np.asarray(y, np.float64)
+    d = np.asarray(d, np.float64)
+    gate, up = gate_up_rows(y.shape[-1])
+    yg, yu = y[..., gate], y[..., up]
+    sg = silu(yg)
+    return sg * yu, SILU_SLOPE_MAX * d[..., gate] * np.abs(yu) + np.abs(sg) * d[..., up]
+
+
+def grouped_gemm_swiglu(x_bf16_bits, offsets, packed, scales, g):
+    """(h, D_h) of the grouped gate_up GEMM with the SiLU(gate) * up epilogue:
+    h [rows, n / 2]; rows of empty segments stay NaN."""
+    y, d = grouped_gemm(x_bf16_bits, offsets, packed, scales, g)
+    return swiglu(y, d)
+
+
+def grouped_gemm_swiglu_sampled(x_bf16_bits, offsets, packed, scales, g, rows_idx, cols_idx):
+    """(h, D_h) at output positions (rows_idx, cols_idx) of the h matrix."""
+    cols_idx = np.asarray(cols_idx, np.int64)
+    gate, up = gate_up_rows(packed.shape[1])
+    rr = np.concatenate([rows_idx, rows_idx])
+    cc = np.concatenate([gate[cols_idx], up[cols_idx]])
+    y, d = grouped_gemm_sampled(x_bf16_bits, offsets, packed, scales, g, rr, cc)
+    m = len(cols_idx)
+    yg, yu, dg, du = y[:m], y[m:], d[:m], d[m:]
+    sg = silu(yg)
+    return sg * yu, SILU_SLOPE_MAX * dg * np.abs(yu) + np.abs(sg) * du

@@ -254,6 +254,34 @@ def extras():
     return out
 
 
+def swiglu_extras(launches):
+    """The gate_up launches with the SiLU(gate) * up epilogue (h [rows, n/2]
+    leaves the kernel), against the plain launch followed by SiLU and the
+    product as separate torch kernels on its output."""
+    import torch
+    import block_scaled_fp4_nibble_amd as nv
+
+    out = {}
+    for L in launches:
+        if not L["name"].startswith("up_"):
+            continue
+        rows, n = L["rows"], L["n"]
+        h = torch.empty((rows, n // 2), dtype=torch.bfloat16, device="cuda")
+        ms = time_fn(lambda: nv.grouped_gemm_swiglu(L["x"], L["off"], L["qw"], out=h), 20, 3)
+
+        def unfused():
+            nv.grouped_gemm(L["x"], L["off"], L["qw"], out=L["y"])
+            torch.mul(torch.nn.functional.silu(L["y"][:, :n // 2]), L["y"][:, n // 2:], out=h)
+        ms_u = time_fn(unfused, 20, 3)
+        nbytes = L["bytes"] - 2 * rows * n + 2 * rows * (n // 2)
+        out["swiglu_" + L["name"]] = {
+            "us": ms * 1e3, "GBps": nbytes / (ms * 1e-3) / 1e9,
+            "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "TFLOPS": L["flops"] / (ms * 1e-3) / 1e12,
+            "unfused_us": ms_u * 1e3}
+    return out
+
+
 def dense_only(m, n, k):
     """One dense GEMM shape: 2 warm-up and 10 timed launches."""
     import torch
@@ -428,6 +456,7 @@ def main():
     }
     if not args.no_extras:
         result["extras"] = extras()
+        result["extras"].update(swiglu_extras(launches))
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -31,7 +31,8 @@ DSTATUS_BAD_OFFSETS = 2
 MAX_EXPERTS = 1024
 
 EXPORTED = [
-    "nvfp4_quantize", "nvfp4_gemm", "nvfp4_grouped_gemm", "nvfp4_quantize_workspace_size",
+    "nvfp4_quantize", "nvfp4_gemm", "nvfp4_grouped_gemm", "nvfp4_grouped_gemm_swiglu",
+    "nvfp4_quantize_workspace_size",
     "nvfp4_gemm_workspace_size", "nvfp4_grouped_gemm_workspace_size",
     "nvfp4_workspace_counter_bytes", "nvfp4_workspace_init", "nvfp4_status_string",
     "nvfp4_version",
@@ -65,6 +66,9 @@ def load_library(path: str = LIB_PATH):
         lib.nvfp4_gemm.restype = I32
         lib.nvfp4_grouped_gemm.argtypes = [P, I64, P, I64, I64, I64, P, P, P, P, I32, P, P, SZ, P]
         lib.nvfp4_grouped_gemm.restype = I32
+        lib.nvfp4_grouped_gemm_swiglu.argtypes = [P, I64, P, I64, I64, I64, P, P, P, P, I32, P, P,
+                                                  SZ, P]
+        lib.nvfp4_grouped_gemm_swiglu.restype = I32
         lib.nvfp4_quantize_workspace_size.argtypes = [I64, I64, I64]
         lib.nvfp4_quantize_workspace_size.restype = SZ
         lib.nvfp4_gemm_workspace_size.argtypes = [I64, I64, I64]
@@ -120,6 +124,14 @@ def nvfp4_grouped_gemm(x, rows, offsets, num_experts, n, k, packed, scales, glob
                                              _ptr(packed), _ptr(scales), _ptr(global_scales),
                                              _ptr(y), out, _ptr(d_status), _ptr(workspace),
                                              ws_bytes, _stream(stream))
+
+
+def nvfp4_grouped_gemm_swiglu(x, rows, offsets, num_experts, n, k, packed, scales,
+                              global_scales, h, out, d_status, workspace, ws_bytes, stream=None):
+    return load_library().nvfp4_grouped_gemm_swiglu(
+        _ptr(x), rows, _ptr(offsets), num_experts, n, k, _ptr(packed), _ptr(scales),
+        _ptr(global_scales), _ptr(h), out, _ptr(d_status), _ptr(workspace), ws_bytes,
+        _stream(stream))
 
 
 def nvfp4_quantize_workspace_size(batch, n, k) -> int:
@@ -257,4 +269,29 @@ def grouped_gemm(x: torch.Tensor, offsets: torch.Tensor, qw: QuantizedWeight,
     _check(nvfp4_grouped_gemm(x, rows, offsets.contiguous(), E, n, k, qw.packed, qw.scales,
                               qw.global_scale, out, code, d_status, ws, nbytes, stream),
            "nvfp4_grouped_gemm")
+    return out
+
+
+def grouped_gemm_swiglu(x: torch.Tensor, offsets: torch.Tensor, qw: QuantizedWeight,
+                        out_dtype=torch.bfloat16, out: torch.Tensor | None = None,
+                        d_status: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """h [rows, n/2] = SiLU(gate) * up of the grouped gate_up product, the
+    weight's rows in 32-row groups of 16 gate rows then the 16 matching up
+    rows (see nvfp4_grouped_gemm_swiglu in include/nvfp4.h)."""
+    x = _bf16_2d_or_3d(x, "x")
+    rows, k = x.shape
+    if qw.packed.dim() != 3 or qw.k != k:
+        raise ValueError("weight must be [E, n, k/2] matching x")
+    E, n, _ = qw.packed.shape
+    if offsets.dtype != torch.int32 or offsets.numel() != E + 1 or not offsets.is_cuda:
+        raise ValueError("offsets must be a device int32 tensor of E+1 entries")
+    code = OUT_F32 if out_dtype == torch.float32 else OUT_BF16
+    if out is None:
+        out = torch.empty((rows, n // 2), dtype=out_dtype, device=x.device)
+    nbytes = nvfp4_grouped_gemm_workspace_size(rows, E, n, k)
+    ws = _gemm_ws.get(nbytes, x.device, stream)
+    _check(nvfp4_grouped_gemm_swiglu(x, rows, offsets.contiguous(), E, n, k, qw.packed,
+                                     qw.scales, qw.global_scale, out, code, d_status, ws, nbytes,
+                                     stream),
+           "nvfp4_grouped_gemm_swiglu")
     return out

@@ -141,7 +141,7 @@ static nvfp4_status_t run_gemm(const void* x, int64_t rows, const int32_t* offse
                                int64_t n, int64_t k, const uint8_t* packed,
                                const uint8_t* scales, const float* g, void* y, nvfp4_out_t out,
                                uint32_t* d_status, void* workspace, size_t ws_bytes,
-                               hipStream_t stream, bool grouped) {
+                               hipStream_t stream, bool grouped, int act = 0) {
   const nvfp4::GemmPlan pl = nvfp4::plan_gemm(rows, E, n, k, grouped, cu_count());
   if (pl.ws_bytes > 0) {
     if (workspace == nullptr || ws_bytes < pl.ws_bytes) return NVFP4_ERR_WORKSPACE;
@@ -168,6 +168,7 @@ static nvfp4_status_t run_gemm(const void* x, int64_t rows, const int32_t* offse
   p.n_tiles = pl.n_tiles;
   p.total_units = -1;
   p.out_f32 = out == NVFP4_OUT_F32 ? 1 : 0;
+  p.act = act;
   return hip_status(nvfp4::launch_gemm(pl, p, stream));
 }
 
@@ -197,6 +198,25 @@ nvfp4_status_t nvfp4_grouped_gemm(const void* x_bf16, int64_t rows,
   return run_gemm(x_bf16, rows, expert_offsets, num_experts, n, k, packed, scales,
                   global_scales, y, out, d_status, workspace, ws_bytes,
                   reinterpret_cast<hipStream_t>(stream), true);
+}
+
+nvfp4_status_t nvfp4_grouped_gemm_swiglu(const void* x_bf16, int64_t rows,
+                                         const int32_t* expert_offsets, int64_t num_experts,
+                                         int64_t n, int64_t k, const uint8_t* packed,
+                                         const uint8_t* scales, const float* global_scales,
+                                         void* h, nvfp4_out_t out, uint32_t* d_status,
+                                         void* workspace, size_t ws_bytes, void* stream) {
+  if (num_experts < 1) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (num_experts > NVFP4_MAX_EXPERTS) return NVFP4_ERR_UNSUPPORTED;
+  if (n % 32 != 0) return NVFP4_ERR_INVALID_ARGUMENT;
+  nvfp4_status_t st =
+      check_gemm_common(x_bf16, rows, n, k, packed, scales, global_scales, h, out);
+  if (st != NVFP4_OK || rows == 0) return st;
+  if (expert_offsets == nullptr) return NVFP4_ERR_INVALID_ARGUMENT;
+  if ((reinterpret_cast<uintptr_t>(expert_offsets) & 3u) != 0) return NVFP4_ERR_MISALIGNED;
+  return run_gemm(x_bf16, rows, expert_offsets, num_experts, n, k, packed, scales,
+                  global_scales, h, out, d_status, workspace, ws_bytes,
+                  reinterpret_cast<hipStream_t>(stream), true, 1);
 }
 
 }  // extern "C"

@@ -39,6 +39,7 @@ struct GemmParams {
   int32_t n_tiles;          // ceil(n / column tile width of the chosen kernel)
   int32_t total_units;      // exact for dense, -1 for grouped (computed on device)
   int32_t out_f32;
+  int32_t act;              // 1: y [rows][n / 2] = SiLU(gate) * up over 32-row gate/up groups
 };
 
 struct GemmPlan {

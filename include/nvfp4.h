@@ -25,7 +25,7 @@
  * finite value (448, resp. 6).  The sign bit is kept for values that round to
  * zero, so -0 encodes as 0x8.
  *
- * Product (nvfp4_gemm, nvfp4_grouped_gemm):
+ * Product (nvfp4_gemm, nvfp4_grouped_gemm, nvfp4_grouped_gemm_swiglu):
  *   y[m][n] = g * sum_k x[m][k] * e2m1(code[n][k]) * decode(s[n][k/16])
  * Each e2m1 * E4M3 product is exact in BF16, so the kernels run BF16 MFMA with
  * FP32 accumulation and apply g once in the epilogue; the BF16 output is the
@@ -136,6 +136,28 @@ nvfp4_status_t nvfp4_grouped_gemm(const void* x_bf16, int64_t rows,
                                   const uint8_t* scales, const float* global_scales,
                                   void* y, nvfp4_out_t out, uint32_t* d_status,
                                   void* workspace, size_t ws_bytes, void* stream);
+
+/* Grouped gate_up GEMM with the SiLU(gate) * up epilogue of a MoE MLP ("The
+ * FP4 Frontier", Finding 5: the fused gate_up GEMM + SiLU of the MoE layer).
+ * Arguments and behaviour are those of nvfp4_grouped_gemm, except:
+ *  - n (even, a multiple of 32) counts the fused weight's rows: each
+ *    expert's packed[e] [n][k/2] and scales[e] [n][k/16] hold them in 32-row
+ *    groups, 16 gate rows followed by the 16 up rows of the same outputs
+ *    (output column c pairs rows 32 (c / 16) + c % 16 and that + 16);
+ *    quantize the fused weight in that row order (one global scale per
+ *    expert covers both halves);
+ *  - the output h [rows][n / 2] (caller-allocated, 16-byte aligned) is
+ *    h[r][c] = SiLU(g y_gate) * (g y_up) with SiLU(v) = v / (1 + e^-v),
+ *    evaluated in FP32 on the FP32 accumulators and rounded once (RNE) for
+ *    NVFP4_OUT_BF16;
+ *  - n % 32 != 0 returns NVFP4_ERR_INVALID_ARGUMENT.
+ * Workspace: nvfp4_grouped_gemm_workspace_size(rows, num_experts, n, k). */
+nvfp4_status_t nvfp4_grouped_gemm_swiglu(const void* x_bf16, int64_t rows,
+                                         const int32_t* expert_offsets, int64_t num_experts,
+                                         int64_t n, int64_t k, const uint8_t* packed,
+                                         const uint8_t* scales, const float* global_scales,
+                                         void* h, nvfp4_out_t out, uint32_t* d_status,
+                                         void* workspace, size_t ws_bytes, void* stream);
 
 /* Workspace sizes (bytes) for the calls above; 0 means none is needed.  The
  * sizes depend on the current device's compute-unit count. */

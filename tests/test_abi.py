@@ -105,6 +105,20 @@ def test_grouped_host_validation(lib):
     assert call(rows=0, offsets=None) == 0
 
 
+def test_grouped_swiglu_host_validation(lib):
+    def call(E=4, offsets=A, rows=8, n=64, k=32):
+        return nv.nvfp4_grouped_gemm_swiglu(A, rows, offsets, E, n, k, A, A, A, A, nv.OUT_BF16,
+                                            None, None, 0, S)
+    assert call(n=48) == 1                   # gate/up rows come in 32-row groups
+    assert call(n=16) == 1
+    assert call(E=0) == 1
+    assert call(E=nv.MAX_EXPERTS + 1) == 3
+    assert call(offsets=None) == 1
+    assert call(offsets=FakePtr(0x10002)) == 2
+    assert call(k=40) == 1
+    assert call(rows=0, offsets=None) == 0
+
+
 def test_quantize_host_validation(lib):
     def call(batch=1, n=4, k=32, w=A, ws=None):
         return nv.nvfp4_quantize(w, batch, n, k, A, A, A, None, ws, 0, S)

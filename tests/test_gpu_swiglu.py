@@ -1,0 +1,154 @@
+"""GPU parity of the grouped gate_up GEMM with the SiLU(gate) * up epilogue.
+
+The fused MoE MLP of "The FP4 Frontier", Finding 5 starts with the gate_up
+grouped GEMM followed by SiLU; here the SiLU(gate) * up product is the GEMM's
+epilogue, so only h [rows, n/2] leaves the kernel.  Parity is against the
+oracle's FP64 product and FP64 SiLU, with the error normalized by D_h, the
+first-order error scale of h (oracle.swiglu): FP32 output within 1e-5, BF16
+within 4e-3, as for the plain GEMM.  Random weights stand for a fused weight
+already in the 32-row gate/up order.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_helpers import (BF16_TOL, F32_TOL, check_close, dev, host, normalized_error,
+                         output_values, require_gpu, sample_positions)
+
+pytestmark = pytest.mark.gpu
+
+
+def to_qw(nv, p, s, g):
+    return nv.QuantizedWeight(dev(p), dev(s), dev(g))
+
+
+def run_swiglu(nv, x, offsets, qw, out_dtype):
+    rows = x.shape[0]
+    out = torch.full((rows, qw.n // 2), float("nan"), dtype=out_dtype, device="cuda")
+    h = nv.grouped_gemm_swiglu(dev(x), dev(offsets.astype(np.int32)), qw, out_dtype=out_dtype,
+                               out=out)
+    torch.cuda.synchronize()
+    return h
+
+
+def case(counts, n, k, seed):
+    E = len(counts)
+    off = np.zeros(E + 1, np.int32)
+    off[1:] = np.cumsum(counts)
+    x = W.normal_bf16((int(off[-1]), k), 1.0, (98, seed, 1))
+    w = W.normal_bf16((E, n, k), 0.05, (98, seed, 2))
+    p, s, g = oracle.quantize(w)
+    return x, off, p, s, g
+
+
+SMALL = [
+    ([3, 0, 17, 1, 0, 40], 64, 576),    # K-phase kernel, ragged tiles, empty experts
+    ([5, 9], 96, 128),                 # a column tile with one 32-row group
+    ([33, 0, 2], 320, 1024),            # several column tiles, a partial one
+    ([7, 1, 20], 64, 80),               # k % 64 != 0: fallback kernel
+    ([70, 0, 5, 33], 256, 2048),        # several row tiles per expert
+]
+
+
+@pytest.mark.parametrize("counts,n,k", SMALL)
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_small_full(counts, n, k, out_dtype):
+    nv = require_gpu()
+    x, off, p, s, g = case(counts, n, k, seed=n + k)
+    h_ref, dh = oracle.grouped_gemm_swiglu(x, off, p, s, g)
+    h = run_swiglu(nv, x, off, to_qw(nv, p, s, g), out_dtype)
+    check_close(h, h_ref, dh, "swiglu %s n=%d k=%d" % (counts, n, k))
+
+
+@pytest.mark.parametrize("splits", [2, 7])
+def test_split_k(splits):
+    # the SiLU(gate) * up epilogue after the split-order reduction
+    nv = require_gpu()
+    x, off, p, s, g = case([6, 0, 30, 2], 128, 1536, seed=3)
+    h_ref, dh = oracle.grouped_gemm_swiglu(x, off, p, s, g)
+    old = os.environ.get("NVFP4_SPLITK")
+    os.environ["NVFP4_SPLITK"] = str(splits)
+    try:
+        h1 = run_swiglu(nv, x, off, to_qw(nv, p, s, g), torch.float32)
+        h2 = run_swiglu(nv, x, off, to_qw(nv, p, s, g), torch.float32)
+    finally:
+        if old is None:
+            os.environ.pop("NVFP4_SPLITK", None)
+        else:
+            os.environ["NVFP4_SPLITK"] = old
+    check_close(h1, h_ref, dh, "swiglu split %d" % splits)
+    assert np.array_equal(host(h1).view(np.uint32), host(h2).view(np.uint32))
+
+
+def test_eight_wave_configuration():
+    nv = require_gpu()
+    x, off, p, s, g = case([12, 3, 0, 25], 512, 768, seed=4)
+    h_ref, dh = oracle.grouped_gemm_swiglu(x, off, p, s, g)
+    old = os.environ.get("NVFP4_KPCFG")
+    os.environ["NVFP4_KPCFG"] = "8"
+    try:
+        h = run_swiglu(nv, x, off, to_qw(nv, p, s, g), torch.float32)
+    finally:
+        if old is None:
+            os.environ.pop("NVFP4_KPCFG", None)
+        else:
+            os.environ["NVFP4_KPCFG"] = old
+    check_close(h, h_ref, dh, "swiglu 8-wave")
+
+
+def test_matches_plain_gemm_then_silu():
+    # same accumulators as the plain grouped GEMM: h equals SiLU(y_gate) * y_up
+    # computed from its FP32 output, up to the FP32 evaluation of SiLU
+    nv = require_gpu()
+    x, off, p, s, g = case([9, 4, 0, 21], 192, 640, seed=5)
+    qw = to_qw(nv, p, s, g)
+    h = output_values(run_swiglu(nv, x, off, qw, torch.float32))
+    y = nv.grouped_gemm(dev(x), dev(off), qw, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    gate, up = oracle.gate_up_rows(192)
+    yv = output_values(y)
+    want = oracle.silu(yv[:, gate]) * yv[:, up]
+    # SiLU runs on the hardware exp2 and reciprocal (relative error ~1e-6)
+    assert np.abs(h - want).max() <= 4e-6 * np.abs(want).max()
+
+
+@pytest.fixture(scope="module")
+def moe_uniform():
+    r, x, w = W.moe_uniform_inputs()
+    p, s, g = oracle.quantize(w)
+    return r, x, p, s, g
+
+
+@pytest.fixture(scope="module")
+def moe_zipf_up():
+    r, x, w = W.moe_zipf_up_inputs()
+    p, s, g = oracle.quantize(w)
+    return r, x, p, s, g
+
+
+def sampled(nv, r, x, p, s, g, out_dtype, seed):
+    h = run_swiglu(nv, x, r.offsets, to_qw(nv, p, s, g), out_dtype)
+    hv = output_values(h)
+    assert np.isfinite(hv).all(), "a routed row was not written"
+    rows, cols = sample_positions(r.rows, hv.shape[1], 2000, seed)
+    h_ref, dh = oracle.grouped_gemm_swiglu_sampled(x, r.offsets, p, s, g, rows, cols)
+    err = normalized_error(hv[rows, cols], h_ref, dh)
+    assert err <= (F32_TOL if out_dtype == torch.float32 else BF16_TOL), err
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_uniform_16_tokens_per_expert(moe_uniform, out_dtype):
+    """gate_up N = 4096 (2 x 2048), K = 6144, ~16 tokens per expert."""
+    nv = require_gpu()
+    r, x, p, s, g = moe_uniform
+    sampled(nv, r, x, p, s, g, out_dtype, seed=21)
+
+
+def test_zipf_64_tokens_per_expert(moe_zipf_up):
+    nv = require_gpu()
+    r, x, p, s, g = moe_zipf_up
+    sampled(nv, r, x, p, s, g, torch.bfloat16, seed=22)

@@ -905,12 +905,13 @@ __global__ __launch_bounds__(KW * 64) void gemm_kp_kernel(GemmParams p) {
 // of 4 x 2 v_mfma_f32_32x32x16_bf16 tiles (FP32 accumulators).  Two waves
 // share each SIMD, so one wave's dequantization, LDS and load-issue work can
 // run while the other's MFMAs occupy the matrix pipeline.  K advances in
-// 64-wide steps through a 3-stage LDS ring holding, per step, the
-// activation tile (256 rows x 128 B) and the packed weight tile (256 rows x
-// 32 B); block scales arrive in windows of 4 steps (256 rows x 16 B).  Per
-// step each wave reads its A and B fragments from LDS, runs 32 MFMAs, and
-// after a barrier writes its 32 weight rows of the next step, dequantized
-// between those MFMAs, into the shared BF16 weight tile (256 rows x 128 B).
+// 64-wide steps.  LDS holds two slots each of the activation tile (256 rows
+// x 128 B) and the packed weight tile (256 rows x 32 B), two BF16 weight
+// tiles (256 rows x 128 B) and two scale windows of 4 steps (256 rows x
+// 16 B).  One barrier per step; after it each wave runs step s's 32 MFMAs
+// from activation slot s % 2 and BF16 tile s % 2, and between them issues
+// the loads of later steps, dequantizes its 32 weight rows of step s + 1 and
+// writes them into BF16 tile (s + 1) % 2.
 //
 // LDS rows of the activation and BF16 weight tiles keep their 16-byte
 // chunk c in slot c ^ ((r >> 1) & 7), so the 32-row fragment reads and the

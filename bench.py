@@ -237,6 +237,25 @@ def extras():
             out["dense_decode_m%d%s" % (m, tag)] = {
                 "us": ms * 1e3, "GBps": dense_bytes(m, n, k) / (ms * 1e-3) / 1e9,
                 "TFLOPS": 2 * m * n * k / (ms * 1e-3) / 1e12}
+        # 16 chained launches (the 4 warm copies in turn) captured once as a
+        # HIP graph and replayed: per-launch time without the host launch path
+        chain = 16
+        nv.gemm(x, ws[0], out=y)  # workspace allocated before capture
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(chain):
+                nv.gemm(x, ws[i % 4], out=y)
+        torch.cuda.current_stream().wait_stream(side)
+        with torch.cuda.graph(graph):
+            for i in range(chain):
+                nv.gemm(x, ws[i % 4], out=y)
+        ms = time_fn(graph.replay, 10, 2) / chain
+        out["dense_decode_m%d_graph" % m] = {
+            "us": ms * 1e3, "GBps": dense_bytes(m, n, k) / (ms * 1e-3) / 1e9}
+        del graph
     del ws, cold
     # 8192^3 dense GEMM and the bulk quantize of its weight
     m = n = k = 8192

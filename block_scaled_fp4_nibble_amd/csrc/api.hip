@@ -143,6 +143,9 @@ static nvfp4_status_t run_gemm(const void* x, int64_t rows, const int32_t* offse
                                uint32_t* d_status, void* workspace, size_t ws_bytes,
                                hipStream_t stream, bool grouped, int act = 0) {
   const nvfp4::GemmPlan pl = nvfp4::plan_gemm(rows, E, n, k, grouped, cu_count());
+  // the SiLU(gate) * up epilogue pairs each wave's column tiles; a kernel
+  // configuration with one tile per wave cannot serve it (never silent)
+  if (act != 0 && !nvfp4::plan_pairs_tiles(pl)) return NVFP4_ERR_UNSUPPORTED;
   if (pl.ws_bytes > 0) {
     if (workspace == nullptr || ws_bytes < pl.ws_bytes) return NVFP4_ERR_WORKSPACE;
     if (!aligned16(workspace)) return NVFP4_ERR_MISALIGNED;

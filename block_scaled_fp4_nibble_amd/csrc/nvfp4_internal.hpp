@@ -60,6 +60,9 @@ struct GemmPlan {
 GemmPlan plan_gemm(int64_t rows, int64_t num_experts, int64_t n, int64_t k, bool grouped,
                    int cu_count);
 hipError_t launch_gemm(const GemmPlan& plan, const GemmParams& p, hipStream_t stream);
+// True when every wave of the planned kernel ends with an even number of
+// 16-column tiles (what the SiLU(gate) * up epilogue needs).
+bool plan_pairs_tiles(const GemmPlan& plan);
 hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t stream);
 
 }  // namespace nvfp4

@@ -1369,8 +1369,13 @@ static int env_int(const char* name, int dflt) {
 constexpr int kLmMinRows = 256;
 constexpr int kMinSplitStages = 7;
 
-static void choose_kernel(GemmPlan& pl, int64_t rows, bool grouped) {
-  if (pl.fast && !grouped && rows >= kLmMinRows && env_int("NVFP4_LM", 1) != 0) {
+static void choose_kernel(GemmPlan& pl, int64_t rows, int64_t n, bool grouped, int cu_count) {
+  // the large-M kernel has no K split: it needs a 256 x 256 output tile for
+  // every CU (at N = 4096, K = 7168 it is 1.2-5x slower than the 64-row
+  // K-phase kernel with split K from 256 to 2048 rows, and faster at 4096)
+  const int64_t lm_tiles = ((rows + kLmBM - 1) / kLmBM) * ((n + kLmBN - 1) / kLmBN);
+  const int lm = env_int("NVFP4_LM", 1);  // 0: never, 2: whenever the shape allows
+  if (pl.fast && !grouped && rows >= kLmMinRows && lm != 0 && (lm == 2 || lm_tiles >= cu_count)) {
     pl.kind = 3; pl.bn = kLmBN; pl.bm = kLmBM;
   } else if (!pl.fast) {
     pl.kind = 0; pl.bn = 256; pl.nslot = 0;
@@ -1440,7 +1445,7 @@ GemmPlan plan_gemm(int64_t rows, int64_t num_experts, int64_t n, int64_t k, bool
   const int force_bm = env_int("NVFP4_BM", 0);
   if (force_bm == 16 || force_bm == 32 || force_bm == 64) bm = force_bm;
   pl.bm = bm;
-  choose_kernel(pl, rows, grouped);
+  choose_kernel(pl, rows, n, grouped, cu_count);
   // the large-M kernel keeps no schedule (dense only)
   pl.dyn_lds = pl.kind == 3 ? 0 : sched_lds_bytes(grouped ? num_experts : 1);
   bm = pl.bm;

@@ -96,10 +96,27 @@ def test_ragged_shapes(m, n, k):
 LARGE_M = [(256, 256, 64), (257, 300, 576), (300, 513, 1088), (511, 1024, 2048), (1000, 129, 4096)]
 
 
+@pytest.fixture
+def lm_mode(request):
+    """NVFP4_LM=2 forces the 256 x 256 large-M kernel for any dense product of
+    256 rows or more (by default it runs only when its tiles fill the CUs)."""
+    old = os.environ.get("NVFP4_LM")
+    if request.param is None:
+        os.environ.pop("NVFP4_LM", None)
+    else:
+        os.environ["NVFP4_LM"] = request.param
+    yield request.param
+    if old is None:
+        os.environ.pop("NVFP4_LM", None)
+    else:
+        os.environ["NVFP4_LM"] = old
+
+
+@pytest.mark.parametrize("lm_mode", ["2", None], indirect=True)
 @pytest.mark.parametrize("m,n,k", LARGE_M)
-def test_large_m_shapes(m, n, k):
-    """Row counts of 256 and more take the 256 x 256 tile path; ragged M, N
-    and one-step K included."""
+def test_large_m_shapes(m, n, k, lm_mode):
+    """Row counts of 256 and more: the 256 x 256 tile path (forced) and the
+    default choice; ragged M, N and one-step K included."""
     nv = require_gpu()
     key = m * 1000003 + n * 1009 + k
     w = W.normal_bf16((n, k), 0.05, (79, key, 0))

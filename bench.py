@@ -108,7 +108,8 @@ def build_workload():
         off = torch.from_numpy(r.offsets.astype(np.int32)).cuda()
         y = torch.empty((r.rows, n), dtype=torch.bfloat16, device="cuda")
         launches.append(dict(name=name, qw=qw, x=x, off=off, y=y, n=n, k=k, rows=r.rows,
-                             counts=r.counts.tolist(), experts=E,
+                             counts=r.counts.tolist(), experts=E, tokens=r.tokens,
+                             row_token=torch.from_numpy(r.row_token.astype(np.int32)).cuda(),
                              bm=bm_for(r.rows, E),
                              flops=2 * r.rows * n * k, bytes=grouped_bytes(r.counts, n, k)))
     torch.cuda.synchronize()
@@ -303,6 +304,32 @@ def swiglu_extras(launches):
     return out
 
 
+def gather_extras(launches):
+    """The up launches reading their routed rows from the token matrix through
+    the routing index, against the plain launch on pre-permuted rows (the
+    step's own form) and against torch's index_select followed by it."""
+    import torch
+    import block_scaled_fp4_nibble_amd as nv
+
+    out = {}
+    for L in launches:
+        if not L["name"].startswith("up_"):
+            continue
+        x_tok = randn_bf16((L["tokens"], L["k"]), 1.0, 500)
+        xp = torch.empty_like(L["x"])
+        ms_g = time_fn(lambda: nv.grouped_gemm_gather(x_tok, L["row_token"], L["off"], L["qw"],
+                                                      out=L["y"]), 20, 3)
+        ms_p = time_fn(lambda: run_launch(L), 20, 3)
+
+        def permuted():
+            torch.index_select(x_tok, 0, L["row_token"], out=xp)
+            nv.grouped_gemm(xp, L["off"], L["qw"], out=L["y"])
+        ms_s = time_fn(permuted, 20, 3)
+        out["gather_" + L["name"]] = {"us": ms_g * 1e3, "prepermuted_us": ms_p * 1e3,
+                                      "index_select_then_gemm_us": ms_s * 1e3}
+    return out
+
+
 def dense_only(m, n, k):
     """One dense GEMM shape: 10 warm-up and 20 timed launches."""
     import torch
@@ -478,6 +505,7 @@ def main():
     if not args.no_extras:
         result["extras"] = extras()
         result["extras"].update(swiglu_extras(launches))
+        result["extras"].update(gather_extras(launches))
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -28,10 +28,12 @@ OUT_BF16 = 0
 OUT_F32 = 1
 DSTATUS_NONFINITE = 1
 DSTATUS_BAD_OFFSETS = 2
+DSTATUS_BAD_INDEX = 4
 MAX_EXPERTS = 1024
 
 EXPORTED = [
     "nvfp4_quantize", "nvfp4_gemm", "nvfp4_grouped_gemm", "nvfp4_grouped_gemm_swiglu",
+    "nvfp4_grouped_gemm_gather",
     "nvfp4_quantize_workspace_size",
     "nvfp4_gemm_workspace_size", "nvfp4_grouped_gemm_workspace_size",
     "nvfp4_workspace_counter_bytes", "nvfp4_workspace_init", "nvfp4_status_string",
@@ -69,6 +71,9 @@ def load_library(path: str = LIB_PATH):
         lib.nvfp4_grouped_gemm_swiglu.argtypes = [P, I64, P, I64, I64, I64, P, P, P, P, I32, P, P,
                                                   SZ, P]
         lib.nvfp4_grouped_gemm_swiglu.restype = I32
+        lib.nvfp4_grouped_gemm_gather.argtypes = [P, I64, P, I64, P, I64, I64, I64, P, P, P, P,
+                                                  I32, I32, P, P, SZ, P]
+        lib.nvfp4_grouped_gemm_gather.restype = I32
         lib.nvfp4_quantize_workspace_size.argtypes = [I64, I64, I64]
         lib.nvfp4_quantize_workspace_size.restype = SZ
         lib.nvfp4_gemm_workspace_size.argtypes = [I64, I64, I64]
@@ -124,6 +129,15 @@ def nvfp4_grouped_gemm(x, rows, offsets, num_experts, n, k, packed, scales, glob
                                              _ptr(packed), _ptr(scales), _ptr(global_scales),
                                              _ptr(y), out, _ptr(d_status), _ptr(workspace),
                                              ws_bytes, _stream(stream))
+
+
+def nvfp4_grouped_gemm_gather(x, x_rows, row_index, rows, offsets, num_experts, n, k, packed,
+                              scales, global_scales, y, out, act, d_status, workspace, ws_bytes,
+                              stream=None):
+    return load_library().nvfp4_grouped_gemm_gather(
+        _ptr(x), x_rows, _ptr(row_index), rows, _ptr(offsets), num_experts, n, k, _ptr(packed),
+        _ptr(scales), _ptr(global_scales), _ptr(y), out, act, _ptr(d_status), _ptr(workspace),
+        ws_bytes, _stream(stream))
 
 
 def nvfp4_grouped_gemm_swiglu(x, rows, offsets, num_experts, n, k, packed, scales,
@@ -294,4 +308,36 @@ def grouped_gemm_swiglu(x: torch.Tensor, offsets: torch.Tensor, qw: QuantizedWei
                                      qw.scales, qw.global_scale, out, code, d_status, ws, nbytes,
                                      stream),
            "nvfp4_grouped_gemm_swiglu")
+    return out
+
+
+def grouped_gemm_gather(x: torch.Tensor, row_index: torch.Tensor, offsets: torch.Tensor,
+                        qw: QuantizedWeight, act: str = "none", out_dtype=torch.bfloat16,
+                        out: torch.Tensor | None = None, d_status: torch.Tensor | None = None,
+                        stream=None) -> torch.Tensor:
+    """Grouped GEMM over routed rows gathered from the token matrix x
+    [tokens, k]: routed row r uses x[row_index[r]].  act="none" returns
+    [rows, n]; act="swiglu" returns SiLU(gate) * up [rows, n/2]."""
+    x = _bf16_2d_or_3d(x, "x")
+    x_rows, k = x.shape
+    if qw.packed.dim() != 3 or qw.k != k:
+        raise ValueError("weight must be [E, n, k/2] matching x")
+    E, n, _ = qw.packed.shape
+    if offsets.dtype != torch.int32 or offsets.numel() != E + 1 or not offsets.is_cuda:
+        raise ValueError("offsets must be a device int32 tensor of E+1 entries")
+    if row_index.dtype != torch.int32 or row_index.dim() != 1 or not row_index.is_cuda:
+        raise ValueError("row_index must be a device int32 vector")
+    rows = row_index.numel()
+    if act not in ("none", "swiglu"):
+        raise ValueError("act must be 'none' or 'swiglu'")
+    code = OUT_F32 if out_dtype == torch.float32 else OUT_BF16
+    ncols = n // 2 if act == "swiglu" else n
+    if out is None:
+        out = torch.empty((rows, ncols), dtype=out_dtype, device=x.device)
+    nbytes = nvfp4_grouped_gemm_workspace_size(rows, E, n, k)
+    ws = _gemm_ws.get(nbytes, x.device, stream)
+    _check(nvfp4_grouped_gemm_gather(x, x_rows, row_index.contiguous(), rows, offsets.contiguous(),
+                                     E, n, k, qw.packed, qw.scales, qw.global_scale, out, code,
+                                     1 if act == "swiglu" else 0, d_status, ws, nbytes, stream),
+           "nvfp4_grouped_gemm_gather")
     return out

@@ -141,7 +141,8 @@ static nvfp4_status_t run_gemm(const void* x, int64_t rows, const int32_t* offse
                                int64_t n, int64_t k, const uint8_t* packed,
                                const uint8_t* scales, const float* g, void* y, nvfp4_out_t out,
                                uint32_t* d_status, void* workspace, size_t ws_bytes,
-                               hipStream_t stream, bool grouped, int act = 0) {
+                               hipStream_t stream, bool grouped, int act = 0,
+                               const int32_t* row_index = nullptr, int64_t x_rows = 0) {
   const nvfp4::GemmPlan pl = nvfp4::plan_gemm(rows, E, n, k, grouped, cu_count());
   // the SiLU(gate) * up epilogue pairs each wave's column tiles; a kernel
   // configuration with one tile per wave cannot serve it (never silent)
@@ -172,6 +173,8 @@ static nvfp4_status_t run_gemm(const void* x, int64_t rows, const int32_t* offse
   p.total_units = -1;
   p.out_f32 = out == NVFP4_OUT_F32 ? 1 : 0;
   p.act = act;
+  p.row_index = row_index;
+  p.x_rows = (int32_t)x_rows;
   return hip_status(nvfp4::launch_gemm(pl, p, stream));
 }
 
@@ -220,6 +223,34 @@ nvfp4_status_t nvfp4_grouped_gemm_swiglu(const void* x_bf16, int64_t rows,
   return run_gemm(x_bf16, rows, expert_offsets, num_experts, n, k, packed, scales,
                   global_scales, h, out, d_status, workspace, ws_bytes,
                   reinterpret_cast<hipStream_t>(stream), true, 1);
+}
+
+nvfp4_status_t nvfp4_grouped_gemm_gather(const void* x_bf16, int64_t x_rows,
+                                         const int32_t* row_index, int64_t rows,
+                                         const int32_t* expert_offsets, int64_t num_experts,
+                                         int64_t n, int64_t k, const uint8_t* packed,
+                                         const uint8_t* scales, const float* global_scales,
+                                         void* y, nvfp4_out_t out, int32_t act,
+                                         uint32_t* d_status, void* workspace, size_t ws_bytes,
+                                         void* stream) {
+  if (num_experts < 1 || x_rows < 0) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (num_experts > NVFP4_MAX_EXPERTS) return NVFP4_ERR_UNSUPPORTED;
+  if (act != 0 && act != 1) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (act == 1 && n % 32 != 0) return NVFP4_ERR_INVALID_ARGUMENT;
+  nvfp4_status_t st =
+      check_gemm_common(x_bf16, rows, n, k, packed, scales, global_scales, y, out);
+  if (st != NVFP4_OK || rows == 0) return st;
+  if (expert_offsets == nullptr || row_index == nullptr || x_rows == 0)
+    return NVFP4_ERR_INVALID_ARGUMENT;
+  if ((reinterpret_cast<uintptr_t>(expert_offsets) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(row_index) & 3u) != 0)
+    return NVFP4_ERR_MISALIGNED;
+  // buffer offsets into x are 32-bit
+  if (x_rows > INT32_MAX || (uint64_t)x_rows * (uint64_t)k * 2u > 0xffffffffull)
+    return NVFP4_ERR_UNSUPPORTED;
+  return run_gemm(x_bf16, rows, expert_offsets, num_experts, n, k, packed, scales,
+                  global_scales, y, out, d_status, workspace, ws_bytes,
+                  reinterpret_cast<hipStream_t>(stream), true, act, row_index, x_rows);
 }
 
 }  // extern "C"

@@ -160,6 +160,21 @@ __device__ __forceinline__ uint32_t sload_u32(const void* base, uint32_t byte_of
   return v;
 }
 
+// Four dwords at byte_off of a buffer through the scalar cache (bounds-
+// checked: bytes past the resource read as zero).  A scalar load counts in
+// lgkmcnt, not in the vector-memory counter the K-phase waits rely on.
+__device__ __forceinline__ u32x4_t sbuffer_load_x4(u32x4_t rsrc, uint32_t byte_off) {
+  rsrc = u32x4_t{(uint32_t)__builtin_amdgcn_readfirstlane(rsrc[0]),
+                 (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[1]),
+                 (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[2]),
+                 (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[3])};
+  u32x4_t v;
+  asm volatile("s_buffer_load_dwordx4 %0, %1, %2\n\ts_waitcnt lgkmcnt(0)"
+               : "=s"(v)
+               : "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(byte_off)));
+  return v;
+}
+
 __device__ __forceinline__ int seg_begin(const GemmParams& p, int e) {
   return p.offsets ? p.offsets[e] : (e == 0 ? 0 : (int)p.rows);
 }
@@ -571,10 +586,12 @@ __device__ __forceinline__ KpU kp_unit(const GemmParams& p, const Unit& u) {
 
 // TAIL: the stage may reach past the end of the unit's K range (only its
 // last stage can).
-template <int BM, int NSLOT, int KW, int BN, bool TAIL = true>
+// G: the unit's activation rows come through a row index (per-unit offsets
+// in u.xg instead of the unit-independent o.x).
+template <int BM, int NSLOT, int KW, int BN, bool TAIL = true, bool G = false>
 __device__ __forceinline__ void kp_issue(uint32_t stage, u32x4_t rw, u32x4_t rx,
                                          const KpOffsets<BM, KW, BN>& o, int kc, int k_end,
-                                         int wave) {
+                                         int wave, uint32_t xg0 = 0, uint32_t xg1 = 0) {
   using L = KpLayout<BM, NSLOT, KW, BN>;
 #pragma unroll
   for (int tt = 0; tt < L::kWPerWave; ++tt)
@@ -583,9 +600,45 @@ __device__ __forceinline__ void kp_issue(uint32_t stage, u32x4_t rw, u32x4_t rx,
 #pragma unroll
   for (int tt = 0; tt < L::kXPerWave; ++tt) {
     const int t = L::kXInstr >= KW ? wave * L::kXPerWave + tt : wave % L::kXInstr;
-    const uint32_t voff = (tail && kc + o.xk[tt] >= k_end) ? kOffNone : o.x[tt];
+    const uint32_t xo = G ? (tt == 0 ? xg0 : xg1) : o.x[tt];
+    const uint32_t voff = (tail && kc + o.xk[tt] >= k_end) ? kOffNone : xo;
     lds_dma16(stage + L::kX + t * 1024, voff, (uint32_t)(kc * 2), rx);
   }
+}
+
+// Activation sources of a unit whose rows come through p.row_index: the
+// buffer spans the whole token matrix, and each lane's load offset follows
+// its row's index.  Load t of a wave covers tile rows 4t .. 4t+3 (lane group
+// lane / 16), so one scalar load brings the four indices of each load.  Rows
+// past the tile, and indices outside [0, x_rows), load nothing (zeros); the
+// latter set NVFP4_DSTATUS_BAD_INDEX.
+template <int BM, int NSLOT, int KW, int BN>
+__device__ __forceinline__ void kp_gather(KpU& s, uint32_t (&xg)[2], const GemmParams& p,
+                                          const Unit& u, int wave, int lane) {
+  using L = KpLayout<BM, NSLOT, KW, BN>;
+  static_assert(L::kXPerWave <= 2, "gather offsets per wave");
+  const uint32_t row_bytes = (uint32_t)p.k * 2u;
+  s.rx = rsrc_words(p.x, (uint32_t)p.x_rows * row_bytes);
+  const u32x4_t ri = rsrc_words(p.row_index + u.row0, (uint32_t)(u.row_end - u.row0) * 4u);
+  const int q = lane >> 4;
+  bool bad = false;
+#pragma unroll
+  for (int tt = 0; tt < L::kXPerWave; ++tt) {
+    const int t = L::kXInstr >= KW ? wave * L::kXPerWave + tt : wave % L::kXInstr;
+    if (4 * t >= u.row_end - u.row0) {  // the load's four rows are all past the tile
+      xg[tt] = kOffNone;
+      continue;
+    }
+    const u32x4_t idx = sbuffer_load_x4(ri, (uint32_t)(16 * t));
+    const uint32_t tok = q == 0 ? idx[0] : (q == 1 ? idx[1] : (q == 2 ? idx[2] : idx[3]));
+    const int r = 4 * t + q;
+    const int g = (lane & 15) ^ (r & 15);
+    const bool row_ok = u.row0 + r < u.row_end;
+    const bool tok_ok = tok < (uint32_t)p.x_rows;  // also rejects negative indices
+    bad |= row_ok && !tok_ok;
+    xg[tt] = (row_ok && tok_ok) ? tok * row_bytes + (uint32_t)(16 * g) : kOffNone;
+  }
+  if (bad && p.d_status != nullptr) atomicOr(p.d_status, NVFP4_DSTATUS_BAD_INDEX);
 }
 
 // Issue the scale window [kw, kw + 128 kWinStages) of the unit (one 1 KB load
@@ -680,10 +733,11 @@ __device__ __forceinline__ void kp_mma(f32x4_t (&acc)[BM / 16][NJ], const KpRegs
 // when it is full), the iterations run in blocks of WS whose waits, window
 // issues and K checks are compile-time constants; the remaining iterations
 // take the general path.
-template <int BM, int NSLOT, int KW, int BN, int NFE>
+template <int BM, int NSLOT, int KW, int BN, int NFE, bool G>
 __device__ __forceinline__ void kp_kloop(f32x4_t (&acc)[BM / 16][2 * BN / KW / 16],
                                          uint8_t* ring, const KpU& cu, int sb0, int wb0, int pf,
-                                         bool ex, const KpU& nx, int pn,
+                                         bool ex, const KpU& nx, int pn, uint32_t cxg0,
+                                         uint32_t cxg1, uint32_t nxg0, uint32_t nxg1,
                                          const KpOffsets<BM, KW, BN>& off, int kp, int ch,
                                          int wave, int lane) {
   using L = KpLayout<BM, NSLOT, KW, BN>;
@@ -706,8 +760,9 @@ __device__ __forceinline__ void kp_kloop(f32x4_t (&acc)[BM / 16][2 * BN / KW / 1
     if (st % WS == 0)
       kp_issue_scales<BM, NSLOT, KW, BN>(ring0 + wbuf(st / WS), cu.rs, off,
                                          cu.k_beg + st * kRingKC, wave);
-    kp_issue<BM, NSLOT, KW, BN>(ring0 + slot(st), cu.rw, cu.rx, off, cu.k_beg + st * kRingKC,
-                                cu.k_end, wave);
+    kp_issue<BM, NSLOT, KW, BN, true, G>(ring0 + slot(st), cu.rw, cu.rx, off,
+                                         cu.k_beg + st * kRingKC, cu.k_end, wave, cxg0,
+                                         cxg1);
   };
   // loads this wave issued after those of stage lo, through stage hi, plus
   // the epilogue stores when stage lo was issued before them
@@ -741,8 +796,9 @@ __device__ __forceinline__ void kp_kloop(f32x4_t (&acc)[BM / 16][2 * BN / KW / 1
     if constexpr ((T + D) % WS == 0)
       kp_issue_scales<BM, NSLOT, KW, BN>(ring0 + wbuf((c + D) / WS), cu.rs, off,
                                          cu.k_beg + (c + D) * kRingKC, wave);
-    kp_issue<BM, NSLOT, KW, BN, false>(ring0 + slot(c + D), cu.rw, cu.rx, off,
-                                       cu.k_beg + (c + D) * kRingKC, cu.k_end, wave);
+    kp_issue<BM, NSLOT, KW, BN, false, G>(ring0 + slot(c + D), cu.rw, cu.rx, off,
+                                          cu.k_beg + (c + D) * kRingKC, cu.k_end, wave, cxg0,
+                                          cxg1);
     kp_read<BM, NJ, NFE, BN, WS>(nxt, ring + slot(c + 1), ring + wbuf((c + 1) / WS), (T + 1) % WS,
                                  true, kp, ch, lane);
     kp_mma<BM, NJ, NFE>(acc, cur);
@@ -763,8 +819,9 @@ __device__ __forceinline__ void kp_kloop(f32x4_t (&acc)[BM / 16][2 * BN / KW / 1
           kp_issue_scales<BM, NSLOT, KW, BN>(ring0 + wbuf(nwin), nx.rs, off, nx.k_beg, wave);
           nx_ops += SPW;
         }
-        kp_issue<BM, NSLOT, KW, BN>(ring0 + slot(c + D), nx.rw, nx.rx, off,
-                                    nx.k_beg + j * kRingKC, nx.k_end, wave);
+        kp_issue<BM, NSLOT, KW, BN, true, G>(ring0 + slot(c + D), nx.rw, nx.rx, off,
+                                             nx.k_beg + j * kRingKC, nx.k_end, wave, nxg0,
+                                             nxg1);
         nx_ops += LS;
       }
       kp_read<BM, NJ, NFE, BN, WS>(nxt, ring + slot(c + 1), ring + wbuf((c + 1) / WS),
@@ -789,7 +846,8 @@ __device__ __forceinline__ void kp_kloop(f32x4_t (&acc)[BM / 16][2 * BN / KW / 1
   }
 }
 
-template <int BM, int NSLOT, int KW, int BN>
+// GATHER: activation rows come through p.row_index (see kp_gather).
+template <int BM, int NSLOT, int KW, int BN, bool GATHER = false>
 __global__ __launch_bounds__(KW * 64) void gemm_kp_kernel(GemmParams p) {
   using L = KpLayout<BM, NSLOT, KW, BN>;
   constexpr int NF = BM / 16;
@@ -816,6 +874,8 @@ __global__ __launch_bounds__(KW * 64) void gemm_kp_kernel(GemmParams p) {
   int round = 0;
   Unit u = decode_unit<BM>(sc, p, first);
   KpU cu = kp_unit<BN>(p, u);
+  uint32_t cxg[2] = {0u, 0u}, nxg[2] = {0u, 0u};
+  if constexpr (GATHER) kp_gather<BM, NSLOT, KW, BN>(cu, cxg, p, u, wave, lane);
   int sb0 = 0, wb0 = 0, pf = 0;
   bool ex = false;
   for (;;) {
@@ -826,6 +886,7 @@ __global__ __launch_bounds__(KW * 64) void gemm_kp_kernel(GemmParams p) {
     if (has_next) {
       un = decode_unit<BM>(sc, p, nu);
       nx = kp_unit<BN>(p, un);
+      if constexpr (GATHER) kp_gather<BM, NSLOT, KW, BN>(nx, nxg, p, un, wave, lane);
     }
     const int pn = (has_next && can_pf && cu.nch >= NSLOT) ? min(L::kPrefetch, nx.nch) : 0;
     const float gv = __uint_as_float(sload_u32(p.g, 4u * (uint32_t)u.e));
@@ -839,8 +900,8 @@ __global__ __launch_bounds__(KW * 64) void gemm_kp_kernel(GemmParams p) {
       for (int j = 0; j < NJ; ++j) acc[f][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
 #define NVFP4_KLOOP(NFE)                                                                         \
-  kp_kloop<BM, NSLOT, KW, BN, NFE>(acc, ring, cu, sb0, wb0, pf, ex, nx, pn, off, kp, ch, wave, \
-                                   lane)
+  kp_kloop<BM, NSLOT, KW, BN, NFE, GATHER>(acc, ring, cu, sb0, wb0, pf, ex, nx, pn, cxg[0], \
+                                           cxg[1], nxg[0], nxg[1], off, kp, ch, wave, lane)
     switch (nf) {
       case 1: NVFP4_KLOOP(1); break;
       case 2: NVFP4_KLOOP(NF >= 2 ? 2 : NF); break;
@@ -893,6 +954,8 @@ __global__ __launch_bounds__(KW * 64) void gemm_kp_kernel(GemmParams p) {
     ex = pn > 0;
     u = un;
     cu = nx;
+    cxg[0] = nxg[0];
+    cxg[1] = nxg[1];
     ++round;
   }
 }
@@ -1211,7 +1274,7 @@ __device__ __forceinline__ void load_wtile(WTile& t, __amdgpu_buffer_rsrc_t rw,
 // Activation chunk [row0, row0 + BM) x [kc, kc + 256): 16-byte pieces, one
 // per thread per pass, zero outside the segment / split.
 template <int BM>
-__device__ __forceinline__ void load_xtile(u32x4_t (&xr)[BM / 8], const uint16_t* __restrict__ x,
+__device__ __forceinline__ void load_xtile(u32x4_t (&xr)[BM / 8], const GemmParams& p,
                                            int row0, int row_end, int K, int kc, int k_end,
                                            int tid) {
 #pragma unroll
@@ -1220,8 +1283,19 @@ __device__ __forceinline__ void load_xtile(u32x4_t (&xr)[BM / 8], const uint16_t
     const int grow = row0 + (pc >> 5);
     const int kk = kc + (pc & 31) * 8;
     xr[pass] = u32x4_t{0u, 0u, 0u, 0u};
-    if (grow < row_end && kk < k_end)
-      xr[pass] = *reinterpret_cast<const u32x4_t*>(x + (int64_t)grow * K + kk);
+    if (grow < row_end && kk < k_end) {
+      // routed row grow reads token row row_index[grow] when an index is given
+      int64_t xrow = grow;
+      if (p.row_index != nullptr) {
+        const uint32_t tok = (uint32_t)p.row_index[grow];
+        if (tok >= (uint32_t)p.x_rows) {
+          if (kk == kc && p.d_status != nullptr) atomicOr(p.d_status, NVFP4_DSTATUS_BAD_INDEX);
+          continue;
+        }
+        xrow = tok;
+      }
+      xr[pass] = *reinterpret_cast<const u32x4_t*>(p.x + xrow * K + kk);
+    }
   }
 }
 
@@ -1298,7 +1372,7 @@ __global__ __launch_bounds__(kRegThreads) void gemm_reg_kernel(GemmParams p) {
     WTile wa, wb;
     u32x4_t xr[BM / 8];
     load_wtile(wa, rw, rs, nrow, K, u.k_beg + 64 * q, u.k_end);
-    load_xtile<BM>(xr, p.x, u.row0, u.row_end, K, u.k_beg, u.k_end, tid);
+    load_xtile<BM>(xr, p, u.row0, u.row_end, K, u.k_beg, u.k_end, tid);
     store_xtile<BM>(xs[0], xr, tid);
     __syncthreads();
     for (int c = 0; c < nch; c += 2) {
@@ -1306,7 +1380,7 @@ __global__ __launch_bounds__(kRegThreads) void gemm_reg_kernel(GemmParams p) {
       const bool more1 = c + 1 < nch;
       if (more1) {
         load_wtile(wb, rw, rs, nrow, K, kc + kKC + 64 * q, u.k_end);
-        load_xtile<BM>(xr, p.x, u.row0, u.row_end, K, kc + kKC, u.k_end, tid);
+        load_xtile<BM>(xr, p, u.row0, u.row_end, K, kc + kKC, u.k_end, tid);
       }
       reg_compute<BM>(acc, xs[0], wa, q, r16);
       if (more1) store_xtile<BM>(xs[1], xr, tid);
@@ -1315,7 +1389,7 @@ __global__ __launch_bounds__(kRegThreads) void gemm_reg_kernel(GemmParams p) {
       const bool more2 = c + 2 < nch;
       if (more2) {
         load_wtile(wa, rw, rs, nrow, K, kc + 2 * kKC + 64 * q, u.k_end);
-        load_xtile<BM>(xr, p.x, u.row0, u.row_end, K, kc + 2 * kKC, u.k_end, tid);
+        load_xtile<BM>(xr, p, u.row0, u.row_end, K, kc + 2 * kKC, u.k_end, tid);
       }
       reg_compute<BM>(acc, xs[1], wb, q, r16);
       if (more2) store_xtile<BM>(xs[0], xr, tid);
@@ -1498,8 +1572,15 @@ bool plan_pairs_tiles(const GemmPlan& pl) {
 
 hipError_t launch_gemm(const GemmPlan& pl, const GemmParams& p, hipStream_t stream) {
   dim3 grid(pl.grid);
-#define NVFP4_KP(BM, NS, KW, BN) \
-  hipLaunchKernelGGL((gemm_kp_kernel<BM, NS, KW, BN>), grid, dim3(KW * 64), pl.dyn_lds, stream, p)
+#define NVFP4_KP(BM, NS, KW, BN)                                                           \
+  do {                                                                                     \
+    if (p.row_index != nullptr)                                                            \
+      hipLaunchKernelGGL((gemm_kp_kernel<BM, NS, KW, BN, true>), grid, dim3(KW * 64),      \
+                         pl.dyn_lds, stream, p);                                           \
+    else                                                                                   \
+      hipLaunchKernelGGL((gemm_kp_kernel<BM, NS, KW, BN>), grid, dim3(KW * 64), pl.dyn_lds, \
+                         stream, p);                                                       \
+  } while (0)
   if (pl.kind == 3) {
     hipLaunchKernelGGL(gemm_lm_kernel, grid, dim3(LmLayout::kWaves * 64), 0, stream, p);
   } else if (pl.kind == 1) {

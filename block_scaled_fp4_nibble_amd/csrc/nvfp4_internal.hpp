@@ -40,6 +40,8 @@ struct GemmParams {
   int32_t total_units;      // exact for dense, -1 for grouped (computed on device)
   int32_t out_f32;
   int32_t act;              // 1: y [rows][n / 2] = SiLU(gate) * up over 32-row gate/up groups
+  const int32_t* row_index; // [rows]: routed row r reads x row row_index[r]; nullptr: row r
+  int32_t x_rows;           // rows of x when row_index is given
 };
 
 struct GemmPlan {

@@ -25,7 +25,8 @@
  * finite value (448, resp. 6).  The sign bit is kept for values that round to
  * zero, so -0 encodes as 0x8.
  *
- * Product (nvfp4_gemm, nvfp4_grouped_gemm, nvfp4_grouped_gemm_swiglu):
+ * Product (nvfp4_gemm, nvfp4_grouped_gemm, nvfp4_grouped_gemm_swiglu,
+ * nvfp4_grouped_gemm_gather):
  *   y[m][n] = g * sum_k x[m][k] * e2m1(code[n][k]) * decode(s[n][k/16])
  * Each e2m1 * E4M3 product is exact in BF16, so the kernels run BF16 MFMA with
  * FP32 accumulation and apply g once in the epilogue; the BF16 output is the
@@ -63,7 +64,9 @@
  *    `d_status` (may be NULL): NVFP4_DSTATUS_NONFINITE (quantize saw a NaN
  *    or infinity; outputs for that tensor are unspecified) and
  *    NVFP4_DSTATUS_BAD_OFFSETS (grouped GEMM saw offsets that are not a
- *    non-decreasing prefix array from 0 to rows; nothing is written to y).
+ *    non-decreasing prefix array from 0 to rows; nothing is written to y)
+ *    and NVFP4_DSTATUS_BAD_INDEX (a gathered row's index lies outside
+ *    [0, x_rows); that row computes as if its activations were zero).
  *    Bits are only ever set (atomic OR), never cleared, by the library.
  *  - Workspace: a device buffer of at least the size the matching
  *    *_workspace_size() function returns (0: pass NULL).  For the two GEMM
@@ -97,6 +100,7 @@ typedef enum { NVFP4_OUT_BF16 = 0, NVFP4_OUT_F32 = 1 } nvfp4_out_t;
 
 #define NVFP4_DSTATUS_NONFINITE 1u
 #define NVFP4_DSTATUS_BAD_OFFSETS 2u
+#define NVFP4_DSTATUS_BAD_INDEX 4u
 
 /* Largest number of experts nvfp4_grouped_gemm accepts. */
 #define NVFP4_MAX_EXPERTS 1024
@@ -158,6 +162,27 @@ nvfp4_status_t nvfp4_grouped_gemm_swiglu(const void* x_bf16, int64_t rows,
                                          const uint8_t* scales, const float* global_scales,
                                          void* h, nvfp4_out_t out, uint32_t* d_status,
                                          void* workspace, size_t ws_bytes, void* stream);
+
+/* Grouped GEMM whose rows are gathered through an index (routing-aware MoE
+ * input, with no permuted copy of the activations): routed row r (rows in
+ * expert order, segments as in nvfp4_grouped_gemm) computes with token row
+ * x[row_index[r]] of x [x_rows][k]; y keeps the routed order.  act = 0 gives
+ * y [rows][n] as nvfp4_grouped_gemm, act = 1 gives h [rows][n / 2] as
+ * nvfp4_grouped_gemm_swiglu (same row-order requirement, n % 32 == 0).
+ * row_index: device int32 [rows], 4-byte aligned; an index outside
+ * [0, x_rows) sets NVFP4_DSTATUS_BAD_INDEX and that row computes as if its
+ * activations were zero.  x_rows * k * 2 must fit in 32 bits (else
+ * NVFP4_ERR_UNSUPPORTED).  Workspace: nvfp4_grouped_gemm_workspace_size(rows,
+ * num_experts, n, k).  The gather is the routing-aware read of the fused MoE
+ * layer ("The FP4 Frontier", Finding 5: one grouped GEMM over all experts). */
+nvfp4_status_t nvfp4_grouped_gemm_gather(const void* x_bf16, int64_t x_rows,
+                                         const int32_t* row_index, int64_t rows,
+                                         const int32_t* expert_offsets, int64_t num_experts,
+                                         int64_t n, int64_t k, const uint8_t* packed,
+                                         const uint8_t* scales, const float* global_scales,
+                                         void* y, nvfp4_out_t out, int32_t act,
+                                         uint32_t* d_status, void* workspace, size_t ws_bytes,
+                                         void* stream);
 
 /* Workspace sizes (bytes) for the calls above; 0 means none is needed.  The
  * sizes depend on the current device's compute-unit count. */

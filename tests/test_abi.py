@@ -119,6 +119,20 @@ def test_grouped_swiglu_host_validation(lib):
     assert call(rows=0, offsets=None) == 0
 
 
+def test_grouped_gather_host_validation(lib):
+    def call(E=4, offsets=A, idx=A, rows=8, x_rows=16, n=64, k=32, act=0):
+        return nv.nvfp4_grouped_gemm_gather(A, x_rows, idx, rows, offsets, E, n, k, A, A, A, A,
+                                            nv.OUT_BF16, act, None, None, 0, S)
+    assert call(idx=None) == 1
+    assert call(x_rows=0) == 1
+    assert call(act=2) == 1
+    assert call(act=1, n=48) == 1
+    assert call(idx=FakePtr(0x10002)) == 2
+    assert call(E=nv.MAX_EXPERTS + 1) == 3
+    assert call(x_rows=1 << 20, k=4096) == 3   # activation offsets exceed 32 bits
+    assert call(rows=0, offsets=None, idx=None) == 0
+
+
 def test_quantize_host_validation(lib):
     def call(batch=1, n=4, k=32, w=A, ws=None):
         return nv.nvfp4_quantize(w, batch, n, k, A, A, A, None, ws, 0, S)

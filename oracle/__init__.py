@@ -320,3 +320,30 @@ def grouped_gemm_swiglu_sampled(x_bf16_bits, offsets, packed, scales, g, rows_id
     yg, yu, dg, du = y[:m], y[m:], d[:m], d[m:]
     sg = silu(yg)
     return sg * yu, SILU_SLOPE_MAX * dg * np.abs(yu) + np.abs(sg) * du
+
+
+# ---- MoE combine -----------------------------------------------------------------
+#
+# The scatter half of the routing-aware MoE layer ("The FP4 Frontier",
+# Finding 5): each token's output is the router-weighted sum of the outputs of
+# its top-k routed rows.  The pages give no formula; the plain reading is
+# out[t] = sum_j w[t, j] * y[rows[t, j]], rows[t, j] < 0 meaning "no row".
+
+
+def moe_combine(y, token_rows, weights):
+    """out [tokens, n] and its error scale D = sum_j |w[t, j] * y[rows[t, j]]|,
+    both float64; y [rows, n] as float64 values."""
+    y = np.asarray(y, np.float64)
+    token_rows = np.asarray(token_rows, np.int64)
+    weights = np.asarray(weights, np.float64)
+    tokens, topk = token_rows.shape
+    out = np.zeros((tokens, y.shape[1]), np.float64)
+    d = np.zeros_like(out)
+    for t in range(tokens):
+        for j in range(topk):
+            r = token_rows[t, j]
+            if r < 0:
+                continue
+            out[t] += weights[t, j] * y[r]
+            d[t] += np.abs(weights[t, j] * y[r])
+    return out, d

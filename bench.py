@@ -342,6 +342,42 @@ def gather_extras(launches):
     return out
 
 
+def combine_extras(launches):
+    """The MoE combine after the down launch: each token's router-weighted sum
+    of its routed rows, against torch's gather-multiply-sum of the same."""
+    import numpy as np
+    import torch
+    import block_scaled_fp4_nibble_amd as nv
+    import workloads as W
+
+    out = {}
+    for L in launches:
+        if not L["name"].startswith("down_"):
+            continue
+        r = W.moe_zipf_routing()
+        assert r.rows == L["rows"]
+        tr = torch.from_numpy(r.token_rows()).cuda()
+        wts = torch.rand((r.tokens, r.topk), generator=torch.Generator("cuda").manual_seed(600),
+                         device="cuda")
+        o = torch.empty((r.tokens, L["n"]), dtype=torch.bfloat16, device="cuda")
+        y = L["y"]
+
+        def ours():
+            nv.moe_combine(y, tr, wts, out=o)
+
+        def torch_ref():
+            (y[tr].float() * wts[..., None]).sum(1).to(torch.bfloat16)
+        ms_c = ms_t = float("inf")
+        for _ in range(2):
+            ms_c = min(ms_c, time_fn(ours, 50, 5))
+            ms_t = min(ms_t, time_fn(torch_ref, 20, 3))
+        nbytes = (r.rows * L["n"] + r.tokens * L["n"]) * 2 + r.rows * 8
+        out["combine_" + L["name"]] = {"us": ms_c * 1e3, "GBps": nbytes / (ms_c * 1e-3) / 1e9,
+                                       "frac_of_hbm": nbytes / (ms_c * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                                       "bytes": nbytes, "torch_gather_mul_sum_us": ms_t * 1e3}
+    return out
+
+
 def dense_only(m, n, k):
     """One dense GEMM shape: 10 warm-up and 20 timed launches."""
     import torch
@@ -519,6 +555,7 @@ def main():
         # extras() the clock runs lower for a while
         ex = swiglu_extras(launches)
         ex.update(gather_extras(launches))
+        ex.update(combine_extras(launches))
         ex.update(extras())
         result["extras"] = ex
     if not args.no_cpu_baseline:

@@ -33,7 +33,7 @@ MAX_EXPERTS = 1024
 
 EXPORTED = [
     "nvfp4_quantize", "nvfp4_gemm", "nvfp4_grouped_gemm", "nvfp4_grouped_gemm_swiglu",
-    "nvfp4_grouped_gemm_gather",
+    "nvfp4_grouped_gemm_gather", "nvfp4_moe_combine",
     "nvfp4_quantize_workspace_size",
     "nvfp4_gemm_workspace_size", "nvfp4_grouped_gemm_workspace_size",
     "nvfp4_workspace_counter_bytes", "nvfp4_workspace_init", "nvfp4_status_string",
@@ -74,6 +74,8 @@ def load_library(path: str = LIB_PATH):
         lib.nvfp4_grouped_gemm_gather.argtypes = [P, I64, P, I64, P, I64, I64, I64, P, P, P, P,
                                                   I32, I32, P, P, SZ, P]
         lib.nvfp4_grouped_gemm_gather.restype = I32
+        lib.nvfp4_moe_combine.argtypes = [P, I32, I64, P, P, I64, I64, I64, P, I32, P, P]
+        lib.nvfp4_moe_combine.restype = I32
         lib.nvfp4_quantize_workspace_size.argtypes = [I64, I64, I64]
         lib.nvfp4_quantize_workspace_size.restype = SZ
         lib.nvfp4_gemm_workspace_size.argtypes = [I64, I64, I64]
@@ -129,6 +131,13 @@ def nvfp4_grouped_gemm(x, rows, offsets, num_experts, n, k, packed, scales, glob
                                              _ptr(packed), _ptr(scales), _ptr(global_scales),
                                              _ptr(y), out, _ptr(d_status), _ptr(workspace),
                                              ws_bytes, _stream(stream))
+
+
+def nvfp4_moe_combine(y, y_type, rows, token_rows, weights, tokens, topk, n, out, out_type,
+                      d_status, stream=None):
+    return load_library().nvfp4_moe_combine(_ptr(y), y_type, rows, _ptr(token_rows),
+                                            _ptr(weights), tokens, topk, n, _ptr(out), out_type,
+                                            _ptr(d_status), _stream(stream))
 
 
 def nvfp4_grouped_gemm_gather(x, x_rows, row_index, rows, offsets, num_experts, n, k, packed,
@@ -340,4 +349,27 @@ def grouped_gemm_gather(x: torch.Tensor, row_index: torch.Tensor, offsets: torch
                                      E, n, k, qw.packed, qw.scales, qw.global_scale, out, code,
                                      1 if act == "swiglu" else 0, d_status, ws, nbytes, stream),
            "nvfp4_grouped_gemm_gather")
+    return out
+
+
+def moe_combine(y: torch.Tensor, token_rows: torch.Tensor, weights: torch.Tensor,
+                out_dtype=torch.bfloat16, out: torch.Tensor | None = None,
+                d_status: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """out [tokens, n] = sum_j weights[t, j] * y[token_rows[t, j]] (router-weighted
+    sum of each token's routed rows; negative ids are empty slots)."""
+    if y.dtype not in (torch.bfloat16, torch.float32) or y.dim() != 2 or not y.is_cuda:
+        raise ValueError("y must be a 2-D bf16 or float32 device tensor")
+    if token_rows.dtype != torch.int32 or token_rows.dim() != 2 or not token_rows.is_cuda:
+        raise ValueError("token_rows must be a [tokens, topk] device int32 tensor")
+    if weights.dtype != torch.float32 or weights.shape != token_rows.shape or not weights.is_cuda:
+        raise ValueError("weights must be a float32 device tensor shaped like token_rows")
+    y = y.contiguous()
+    rows, n = y.shape
+    tokens, topk = token_rows.shape
+    if out is None:
+        out = torch.empty((tokens, n), dtype=out_dtype, device=y.device)
+    _check(nvfp4_moe_combine(y, OUT_F32 if y.dtype == torch.float32 else OUT_BF16, rows,
+                             token_rows.contiguous(), weights.contiguous(), tokens, topk, n, out,
+                             OUT_F32 if out.dtype == torch.float32 else OUT_BF16, d_status,
+                             stream), "nvfp4_moe_combine")
     return out

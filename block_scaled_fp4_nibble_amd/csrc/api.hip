@@ -225,6 +225,28 @@ nvfp4_status_t nvfp4_grouped_gemm_swiglu(const void* x_bf16, int64_t rows,
                   reinterpret_cast<hipStream_t>(stream), true, 1);
 }
 
+nvfp4_status_t nvfp4_moe_combine(const void* y, nvfp4_out_t y_type, int64_t rows,
+                                 const int32_t* token_rows, const float* weights,
+                                 int64_t tokens, int64_t topk, int64_t n, void* out,
+                                 nvfp4_out_t out_type, uint32_t* d_status, void* stream) {
+  if (tokens < 0 || rows < 0 || n < 1 || n % 8 != 0 || topk < 1 || topk > 64)
+    return NVFP4_ERR_INVALID_ARGUMENT;
+  if ((y_type != NVFP4_OUT_BF16 && y_type != NVFP4_OUT_F32) ||
+      (out_type != NVFP4_OUT_BF16 && out_type != NVFP4_OUT_F32))
+    return NVFP4_ERR_INVALID_ARGUMENT;
+  if (n >= kInt31 || rows >= kInt31 || tokens >= kInt31 / 64 ||
+      tokens * ((n + 2047) / 2048) >= kInt31)  // one workgroup per 2048-column chunk
+    return NVFP4_ERR_UNSUPPORTED;
+  if (tokens == 0) return NVFP4_OK;
+  if (!y || !token_rows || !weights || !out) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (!aligned16(y) || !aligned16(out) || (reinterpret_cast<uintptr_t>(token_rows) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(weights) & 3u) != 0)
+    return NVFP4_ERR_MISALIGNED;
+  return hip_status(nvfp4::launch_moe_combine(
+      y, y_type == NVFP4_OUT_F32, rows, token_rows, weights, tokens, (int)topk, (int)n, out,
+      out_type == NVFP4_OUT_F32, d_status, reinterpret_cast<hipStream_t>(stream)));
+}
+
 nvfp4_status_t nvfp4_grouped_gemm_gather(const void* x_bf16, int64_t x_rows,
                                          const int32_t* row_index, int64_t rows,
                                          const int32_t* expert_offsets, int64_t num_experts,

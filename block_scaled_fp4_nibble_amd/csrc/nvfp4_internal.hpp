@@ -67,4 +67,9 @@ hipError_t launch_gemm(const GemmPlan& plan, const GemmParams& p, hipStream_t st
 bool plan_pairs_tiles(const GemmPlan& plan);
 hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t stream);
 
+// ---- MoE combine -----------------------------------------------------------
+hipError_t launch_moe_combine(const void* y, bool y_f32, int64_t rows, const int32_t* token_rows,
+                              const float* w, int64_t tokens, int topk, int n, void* out,
+                              bool out_f32, uint32_t* d_status, hipStream_t stream);
+
 }  // namespace nvfp4

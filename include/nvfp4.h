@@ -184,6 +184,23 @@ nvfp4_status_t nvfp4_grouped_gemm_gather(const void* x_bf16, int64_t x_rows,
                                          uint32_t* d_status, void* workspace, size_t ws_bytes,
                                          void* stream);
 
+/* MoE combine, the scatter half of the routing-aware MoE layer ("The FP4
+ * Frontier", Finding 5): out[t][c] = sum_j weights[t][j] * y[token_rows[t][j]][c]
+ * for t < tokens, j < topk, summed in slot order in FP32 and rounded once
+ * (RNE) for NVFP4_OUT_BF16.  y [rows][n] (y_type: BF16 or F32) holds the
+ * routed rows, e.g. the down projection's output in expert order;
+ * token_rows [tokens][topk] (device int32) names each token's routed rows, a
+ * negative entry meaning an empty slot; weights [tokens][topk] (device FP32)
+ * are the router weights.  out [tokens][n] (out_type).  No atomics: the
+ * result is bitwise reproducible.  n must be a multiple of 8 and y, out
+ * 16-byte aligned; token_rows and weights 4-byte aligned; 1 <= topk <= 64.
+ * A row id >= rows sets NVFP4_DSTATUS_BAD_INDEX and that slot contributes
+ * nothing.  tokens == 0 is a no-op.  No workspace. */
+nvfp4_status_t nvfp4_moe_combine(const void* y, nvfp4_out_t y_type, int64_t rows,
+                                 const int32_t* token_rows, const float* weights,
+                                 int64_t tokens, int64_t topk, int64_t n, void* out,
+                                 nvfp4_out_t out_type, uint32_t* d_status, void* stream);
+
 /* Workspace sizes (bytes) for the calls above; 0 means none is needed.  The
  * sizes depend on the current device's compute-unit count. */
 size_t nvfp4_quantize_workspace_size(int64_t batch, int64_t n, int64_t k);

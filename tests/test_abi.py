@@ -133,6 +133,22 @@ def test_grouped_gather_host_validation(lib):
     assert call(rows=0, offsets=None, idx=None) == 0
 
 
+def test_moe_combine_host_validation(lib):
+    def call(y=A, rows=8, tr=A, w=A, tokens=4, topk=2, n=64, out=A, yt=None, ot=None):
+        yt = nv.OUT_BF16 if yt is None else yt
+        ot = nv.OUT_BF16 if ot is None else ot
+        return nv.nvfp4_moe_combine(y, yt, rows, tr, w, tokens, topk, n, out, ot, None, S)
+    assert call(n=12) == 1                    # columns come in groups of 8
+    assert call(topk=0) == 1
+    assert call(topk=65) == 1
+    assert call(tokens=-1) == 1
+    assert call(yt=7) == 1
+    assert call(tr=None) == 1
+    assert call(y=MIS) == 2
+    assert call(w=FakePtr(0x10002)) == 2
+    assert call(tokens=0, y=None, tr=None, w=None, out=None) == 0
+
+
 def test_quantize_host_validation(lib):
     def call(batch=1, n=4, k=32, w=A, ws=None):
         return nv.nvfp4_quantize(w, batch, n, k, A, A, A, None, ws, 0, S)

@@ -94,6 +94,11 @@ class Routing:
     def rows(self) -> int:
         return int(self.offsets[-1])
 
+    def token_rows(self) -> np.ndarray:
+        """int32 [tokens, topk]: the routed rows of each token, in row order."""
+        order = np.argsort(self.row_token, kind="stable")
+        return order.reshape(self.tokens, self.topk).astype(np.int32)
+
 
 def _sorted_routing(choices: np.ndarray, num_experts: int) -> Routing:
     tokens, topk = choices.shape

@@ -276,15 +276,16 @@ def extras():
     out["quantize_8192x8192"] = {"us": ms * 1e3, "GBps": qbytes / (ms * 1e-3) / 1e9}
     # measured ceilings on this machine, as context for the spec peaks: the BF16
     # GEMM of the same shape through torch (hipBLASLt; contiguous operands)
-    # and a streaming read (a sum over 2 GiB of FP32)
+    # and a device-to-device copy of 1 GiB (bytes read + bytes written)
     wt = w.t().contiguous()
     ms = time_fn(lambda: torch.matmul(x, wt, out=y), 20, 10)
     out["measured_bf16_gemm_8192_cubed"] = {"ms": ms, "TFLOPS": 2 * m * n * k / (ms * 1e-3) / 1e12}
     del wt, w, qw, x, y
-    big = torch.ones(1 << 29, dtype=torch.float32, device="cuda")
-    ms = time_fn(lambda: big.sum(), 10, 3)
-    out["measured_read_2GiB"] = {"us": ms * 1e3, "GBps": big.numel() * 4 / (ms * 1e-3) / 1e9}
-    del big
+    src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    ms = time_fn(lambda: dst.copy_(src), 10, 3)
+    out["measured_copy_1GiB"] = {"us": ms * 1e3, "GBps": 2 * src.numel() / (ms * 1e-3) / 1e9}
+    del src, dst
     return out
 
 

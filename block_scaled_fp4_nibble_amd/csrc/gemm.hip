@@ -1507,6 +1507,22 @@ GemmPlan plan_gemm(int64_t rows, int64_t num_experts, int64_t n, int64_t k, bool
                    int cu_count) {
   GemmPlan pl{};
   pl.fast = (k % 64) == 0;
+  // one to four dense rows: the dot-product kernel, 16 columns per workgroup,
+  // whole K, no workspace (kind 6)
+  if (!grouped && rows >= 1 && rows <= kGemvMaxRows && k % 32 == 0 &&
+      rows * k * 2 <= kGemvMaxXBytes && env_int("NVFP4_GEMV", 1) != 0) {
+    pl.kind = 6;
+    pl.bm = (int)rows;
+    pl.bn = 16;
+    pl.splits = 1;
+    pl.k_split = (int)k;
+    pl.n_tiles = (int)((n + 15) / 16);
+    pl.max_tiles = pl.n_tiles;
+    pl.grid = pl.n_tiles;
+    pl.dyn_lds = (int)(rows * k * 2);
+    pl.ws_bytes = 0;
+    return pl;
+  }
   const int64_t avg = grouped ? (rows + num_experts - 1) / (num_experts > 0 ? num_experts : 1)
                               : rows;
   int bm = avg <= 16 ? 16 : (avg <= 32 ? 32 : 64);
@@ -1571,6 +1587,7 @@ bool plan_pairs_tiles(const GemmPlan& pl) {
 }
 
 hipError_t launch_gemm(const GemmPlan& pl, const GemmParams& p, hipStream_t stream) {
+  if (pl.kind == 6) return launch_gemv(pl, p, stream);
   dim3 grid(pl.grid);
 #define NVFP4_KP(BM, NS, KW, BN)                                                           \
   do {                                                                                     \

@@ -1,0 +1,161 @@
+// gemv.hip -- dense products with one to four token rows (decode).
+//
+// Decode is the bandwidth-bound case ("The FP4 Frontier", Finding 7).  With
+// so few rows a 16-row MFMA tile is mostly padding, and the in-register
+// dequantization (16 VALU instructions per 8 weights) is what bounds the
+// K-phase kernel.  Here the block scale leaves the inner loop instead; with
+// the two scale tiers of "The Blackwell Architectural Split: NVFP4, Attention,
+// and Consumer Silicon", section "Preserving precision" (an E4M3 factor per
+// 16-element block, an FP32 factor per tensor):
+//   y[m][n] = g * sum_b s[n][b] * (sum_{k in b} x[m][k] * e2m1(q[n][k]))
+// The inner sum runs on the packed BF16 dot product: the FP4 convert turns
+// two nibbles into two exact BF16 values (scale operand 1.0), and one
+// v_dot2c_f32_bf16 multiplies them with two activations and adds both
+// products into an FP32 accumulator.  That is about one VALU instruction per
+// weight per row instead of two plus an MFMA share.
+//
+// Layout: one workgroup of 8 waves per 16 output columns.  Lane 4r + c of a
+// wave reads row n0 + r; the four lanes of a row read four consecutive 16-byte
+// chunks (32 weights each, 64 contiguous bytes), the waves take the row's
+// next 128-byte groups in turn, so every chunk of the row is read once and
+// each lane keeps up to kGemvBatch chunks in flight.  The token rows are
+// staged in LDS once.  The partial sums are reduced in a fixed order: chunk
+// order within a lane, the four lanes of a row, then the eight waves.
+#include "nvfp4_internal.hpp"
+#include "device_common.hpp"
+
+namespace nvfp4 {
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+constexpr int kGemvThreads = 512;  // 8 waves
+constexpr int kGemvWaves = kGemvThreads / kWave;
+constexpr int kGemvCols = 16;      // weight rows (output columns) per workgroup
+constexpr int kGemvBatch = 8;      // chunks a lane loads before it multiplies them
+
+template <int M>
+__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemmParams p) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t xl[];  // [M][K] bf16
+  __shared__ float red[kGemvWaves][M][kGemvCols];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int K = p.k, N = p.n;
+  const int n0 = blockIdx.x * kGemvCols;
+  const int r = lane >> 2, cl = lane & 3;
+  const int n = n0 + r;
+  const bool row_ok = n < N;
+  const int C = K / 32;  // 32-weight chunks per row
+  constexpr int kStride = 4 * kGemvWaves;  // chunks between a lane's consecutive chunks
+  const uint8_t* wrow = p.w + (int64_t)(row_ok ? n : 0) * (K / 2);
+  const uint8_t* srow = p.s + (int64_t)(row_ok ? n : 0) * (K / 16);
+  uint4 pk[kGemvBatch];
+  uint32_t sc[kGemvBatch];
+  auto load_batch = [&](int c0) {
+#pragma unroll
+    for (int b = 0; b < kGemvBatch; ++b) {
+      const int c = c0 + kStride * b;
+      if (row_ok && c < C) {
+        pk[b] = *reinterpret_cast<const uint4*>(wrow + 16 * (int64_t)c);
+        sc[b] = *reinterpret_cast<const uint16_t*>(srow + 2 * (int64_t)c);
+      } else {
+        pk[b] = make_uint4(0u, 0u, 0u, 0u);
+        sc[b] = 0u;
+      }
+    }
+  };
+  // the first weight loads go out before the token rows are staged, so the
+  // two latencies overlap
+  int c0 = 4 * wave + cl;
+  load_batch(c0);
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(p.x);
+    uint4* dst = reinterpret_cast<uint4*>(xl);
+    const int nv = M * K / 8;
+    for (int i0 = tid; i0 < nv; i0 += 4 * kGemvThreads) {
+      uint4 t[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (i0 + u * kGemvThreads < nv) t[u] = src[i0 + u * kGemvThreads];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (i0 + u * kGemvThreads < nv) dst[i0 + u * kGemvThreads] = t[u];
+    }
+  }
+  __syncthreads();
+  float acc[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) acc[m] = 0.f;
+  for (; c0 < C; c0 += kStride * kGemvBatch) {
+#pragma unroll
+    for (int b = 0; b < kGemvBatch; ++b) {
+      const int c = c0 + kStride * b;
+      if (c < C) {
+        // the chunk's two blocks: dwords 0-1 and 2-3, scale bytes 0 and 1
+        const float s0 = decode_e4m3<0>(sc[b]), s1 = decode_e4m3<1>(sc[b]);
+        const uint32_t pw[4] = {pk[b].x, pk[b].y, pk[b].z, pk[b].w};
+        bf16x2_t q[16];  // q[4 j + t]: weights 8 j + 2 t and 8 j + 2 t + 1 of the chunk
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          q[4 * j + 0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(pw[j], 1.0f, 0);
+          q[4 * j + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(pw[j], 1.0f, 1);
+          q[4 * j + 2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(pw[j], 1.0f, 2);
+          q[4 * j + 3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(pw[j], 1.0f, 3);
+        }
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          const uint4* xr = reinterpret_cast<const uint4*>(xl + m * K + 32 * c);
+          float part[2] = {0.f, 0.f};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint4 xv = xr[j];  // activations 8 j .. 8 j + 7 of the chunk
+            const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+              part[j >> 1] = __builtin_amdgcn_fdot2_f32_bf16(
+                  q[4 * j + t], __builtin_bit_cast(bf16x2_t, xw[t]), part[j >> 1], false);
+          }
+          acc[m] += s0 * part[0];
+          acc[m] += s1 * part[1];
+        }
+      }
+    }
+    if (c0 + kStride * kGemvBatch < C) load_batch(c0 + kStride * kGemvBatch);
+  }
+  // the four lanes of a row, then the waves, in a fixed order
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    float v = acc[m];
+    v += __shfl_xor(v, 1);
+    v += __shfl_xor(v, 2);
+    if (cl == 0) red[wave][m][r] = v;
+  }
+  __syncthreads();
+  if (tid < M * kGemvCols) {
+    const int m = tid / kGemvCols, rr = tid % kGemvCols;
+    const int col = n0 + rr;
+    if (col < N) {
+      float sum = red[0][m][rr];
+#pragma unroll
+      for (int w = 1; w < kGemvWaves; ++w) sum += red[w][m][rr];
+      const float v = p.g[0] * sum;
+      const int64_t o = (int64_t)m * N + col;
+      if (p.out_f32)
+        static_cast<float*>(p.y)[o] = v;
+      else
+        static_cast<uint16_t*>(p.y)[o] = (uint16_t)float_to_bf16_rne(v);
+    }
+  }
+}
+
+hipError_t launch_gemv(const GemmPlan& pl, const GemmParams& p, hipStream_t stream) {
+  const dim3 grid((unsigned)pl.grid), block(kGemvThreads);
+  switch (pl.bm) {
+    case 1: hipLaunchKernelGGL(gemv_kernel<1>, grid, block, pl.dyn_lds, stream, p); break;
+    case 2: hipLaunchKernelGGL(gemv_kernel<2>, grid, block, pl.dyn_lds, stream, p); break;
+    case 3: hipLaunchKernelGGL(gemv_kernel<3>, grid, block, pl.dyn_lds, stream, p); break;
+    case 4: hipLaunchKernelGGL(gemv_kernel<4>, grid, block, pl.dyn_lds, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

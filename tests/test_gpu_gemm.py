@@ -37,14 +37,18 @@ def run_gemm(nv, x_bits, qw, out_dtype, sentinel=True):
 
 @pytest.fixture
 def splitk(request):
-    """Force a K split through the library's tuning override."""
-    old = os.environ.get("NVFP4_SPLITK")
+    """Force a K split through the library's tuning override (and the K-phase
+    kernel for products of one to four rows, which otherwise take the
+    dot-product kernel and never split K)."""
+    old = {v: os.environ.get(v) for v in ("NVFP4_SPLITK", "NVFP4_GEMV")}
     os.environ["NVFP4_SPLITK"] = str(request.param)
+    os.environ["NVFP4_GEMV"] = "0"
     yield request.param
-    if old is None:
-        os.environ.pop("NVFP4_SPLITK", None)
-    else:
-        os.environ["NVFP4_SPLITK"] = old
+    for v, o in old.items():
+        if o is None:
+            os.environ.pop(v, None)
+        else:
+            os.environ[v] = o
 
 
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])

@@ -10,6 +10,8 @@ the end of every launch, so a captured launch can be replayed.  Each test
 replays several times with eager work and synchronizations in between and
 checks every replay against the eager result.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -52,16 +54,26 @@ def replay_and_compare(fn, outs, reps=4):
             assert np.array_equal(bits(o), w), "replay %d differs from the eager launch" % i
 
 
-def test_dense_decode_split_k_replay():
-    # M = 1 decode runs split-K: partial tiles and arrival counters in the
-    # workspace, reset by the last split of each tile
+@pytest.mark.parametrize("m,gemv", [(1, "1"), (1, "0"), (16, "1")])
+def test_dense_decode_replay(m, gemv):
+    # M = 1 takes the dot-product kernel; with it switched off (and at
+    # M = 16) the decode runs split-K: partial tiles and arrival counters in
+    # the workspace, reset by the last split of each tile
     nv = require_gpu()
     w = W.decode_weight()
     p, s, g = oracle.quantize(w)
     qw = nv.QuantizedWeight(dev(p), dev(s), dev(np.atleast_1d(g).astype(np.float32)))
-    x = dev(W.decode_act(1))
-    y = torch.empty((1, qw.n), dtype=torch.bfloat16, device="cuda")
-    replay_and_compare(lambda: nv.gemm(x, qw, out=y), [y])
+    x = dev(W.decode_act(m))
+    y = torch.empty((m, qw.n), dtype=torch.bfloat16, device="cuda")
+    old = os.environ.get("NVFP4_GEMV")
+    os.environ["NVFP4_GEMV"] = gemv
+    try:
+        replay_and_compare(lambda: nv.gemm(x, qw, out=y), [y])
+    finally:
+        if old is None:
+            os.environ.pop("NVFP4_GEMV", None)
+        else:
+            os.environ["NVFP4_GEMV"] = old
 
 
 def test_grouped_and_swiglu_chain_replay():

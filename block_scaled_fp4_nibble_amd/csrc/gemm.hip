@@ -1523,6 +1523,22 @@ GemmPlan plan_gemm(int64_t rows, int64_t num_experts, int64_t n, int64_t k, bool
     pl.ws_bytes = 0;
     return pl;
   }
+  // five to sixteen dense rows, k % 128 == 0: one MFMA row tile per 16
+  // columns, whole K, every load in flight at once (kind 7, gemv.hip)
+  if (!grouped && rows > kGemvMaxRows && rows <= 16 && k % 128 == 0 &&
+      env_int("NVFP4_GEMV", 1) != 0) {
+    pl.kind = 7;
+    pl.bm = 16;
+    pl.bn = 16;
+    pl.splits = 1;
+    pl.k_split = (int)k;
+    pl.n_tiles = (int)((n + 15) / 16);
+    pl.max_tiles = pl.n_tiles;
+    pl.grid = pl.n_tiles;
+    pl.dyn_lds = 0;
+    pl.ws_bytes = 0;
+    return pl;
+  }
   const int64_t avg = grouped ? (rows + num_experts - 1) / (num_experts > 0 ? num_experts : 1)
                               : rows;
   int bm = avg <= 16 ? 16 : (avg <= 32 ? 32 : 64);
@@ -1587,7 +1603,7 @@ bool plan_pairs_tiles(const GemmPlan& pl) {
 }
 
 hipError_t launch_gemm(const GemmPlan& pl, const GemmParams& p, hipStream_t stream) {
-  if (pl.kind == 6) return launch_gemv(pl, p, stream);
+  if (pl.kind == 6 || pl.kind == 7) return launch_gemv(pl, p, stream);
   dim3 grid(pl.grid);
 #define NVFP4_KP(BM, NS, KW, BN)                                                           \
   do {                                                                                     \

@@ -33,6 +33,26 @@ constexpr int kGemvWaves = kGemvThreads / kWave;
 constexpr int kGemvCols = 16;      // weight rows (output columns) per workgroup
 constexpr int kGemvBatch = 8;      // chunks a lane loads before it multiplies them
 
+// Chunks c0, c0 + STRIDE, ... (kGemvBatch of them) of one weight row: 16
+// packed bytes and two scale bytes each; chunks past the row, and rows past
+// N, read as zero.
+template <int STRIDE>
+__device__ __forceinline__ void gemv_load_batch(uint4 (&pk)[kGemvBatch], uint32_t (&sc)[kGemvBatch],
+                                                const uint8_t* wrow, const uint8_t* srow, int c0,
+                                                int C, bool row_ok) {
+#pragma unroll
+  for (int b = 0; b < kGemvBatch; ++b) {
+    const int c = c0 + STRIDE * b;
+    if (row_ok && c < C) {
+      pk[b] = *reinterpret_cast<const uint4*>(wrow + 16 * (int64_t)c);
+      sc[b] = *reinterpret_cast<const uint16_t*>(srow + 2 * (int64_t)c);
+    } else {
+      pk[b] = make_uint4(0u, 0u, 0u, 0u);
+      sc[b] = 0u;
+    }
+  }
+}
+
 template <int M>
 __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemmParams p) {
   extern __shared__ __attribute__((aligned(16))) uint16_t xl[];  // [M][K] bf16
@@ -49,32 +69,19 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemmParams p) {
   const uint8_t* srow = p.s + (int64_t)(row_ok ? n : 0) * (K / 16);
   uint4 pk[kGemvBatch];
   uint32_t sc[kGemvBatch];
-  auto load_batch = [&](int c0) {
-#pragma unroll
-    for (int b = 0; b < kGemvBatch; ++b) {
-      const int c = c0 + kStride * b;
-      if (row_ok && c < C) {
-        pk[b] = *reinterpret_cast<const uint4*>(wrow + 16 * (int64_t)c);
-        sc[b] = *reinterpret_cast<const uint16_t*>(srow + 2 * (int64_t)c);
-      } else {
-        pk[b] = make_uint4(0u, 0u, 0u, 0u);
-        sc[b] = 0u;
-      }
-    }
-  };
-  // the first weight loads go out before the token rows are staged, so the
-  // two latencies overlap
+  // the first weight loads go out before the token rows are staged in LDS
   int c0 = 4 * wave + cl;
-  load_batch(c0);
+  gemv_load_batch<kStride>(pk, sc, wrow, srow, c0, C, row_ok);
   {
     const uint4* src = reinterpret_cast<const uint4*>(p.x);
     uint4* dst = reinterpret_cast<uint4*>(xl);
     const int nv = M * K / 8;
     for (int i0 = tid; i0 < nv; i0 += 4 * kGemvThreads) {
+      // four loads in flight (indexes past the end re-read the last vector,
+      // whose store is skipped)
       uint4 t[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (i0 + u * kGemvThreads < nv) t[u] = src[i0 + u * kGemvThreads];
+      for (int u = 0; u < 4; ++u) t[u] = src[min(i0 + u * kGemvThreads, nv - 1)];
 #pragma unroll
       for (int u = 0; u < 4; ++u)
         if (i0 + u * kGemvThreads < nv) dst[i0 + u * kGemvThreads] = t[u];
@@ -118,7 +125,8 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemmParams p) {
         }
       }
     }
-    if (c0 + kStride * kGemvBatch < C) load_batch(c0 + kStride * kGemvBatch);
+    if (c0 + kStride * kGemvBatch < C)
+      gemv_load_batch<kStride>(pk, sc, wrow, srow, c0 + kStride * kGemvBatch, C, row_ok);
   }
   // the four lanes of a row, then the waves, in a fixed order
 #pragma unroll
@@ -146,7 +154,101 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemmParams p) {
   }
 }
 
+// ---- 5 to 16 rows: one MFMA row tile, whole K per workgroup -------------------
+//
+// Above four rows the per-row dot products cost more than one BF16 MFMA row
+// tile, but the K-phase kernel's latency structure (a ring of 128-deep stages,
+// split K with a partial-tile hand-off) still dominates at decode sizes.  This
+// kernel keeps every load of a workgroup in flight at once instead: one
+// workgroup of 8 waves per 16 output columns, whole K; wave w takes the
+// 128-deep K groups j = w, w + 8, ...  Within a group, lane (n, g) = (l % 16,
+// l / 16) loads 16 contiguous bytes of weight row n (K = 128 j + 32 g .. + 31),
+// their two scale bytes, and the matching 64 activation bytes of token row
+// l % 16 straight from global memory (the token rows are read by every
+// workgroup and stay in L2).  The MFMA's 32 K slots are a permutation of real
+// K -- slot 8 g + i of step t is K = 128 j + 32 g + 8 t + i -- applied to both
+// operands alike, so the product is unchanged.  Partial tiles of the 8 waves
+// are summed in wave order through LDS.
+constexpr int kDecodeJB = 8;  // 128-deep K groups a lane loads before it multiplies them
+
+__global__ __launch_bounds__(kGemvThreads) void decode_mfma_kernel(GemmParams p) {
+  __shared__ f32x4_t red[kGemvWaves][kWave];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int K = p.k, N = p.n, M = (int)p.rows;
+  const int n0 = blockIdx.x * kGemvCols;
+  const int c16 = lane & 15, g = lane >> 4;
+  const int n = n0 + c16;
+  const bool col_ok = n < N, row_ok = c16 < M;
+  const int J = K / 128;
+  const uint8_t* wrow = p.w + (int64_t)(col_ok ? n : 0) * (K / 2) + 16 * g;
+  const uint8_t* srow = p.s + (int64_t)(col_ok ? n : 0) * (K / 16) + 2 * g;
+  const uint16_t* xrow = p.x + (int64_t)(row_ok ? c16 : 0) * K + 32 * g;
+  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int j0 = wave; j0 < J; j0 += kGemvWaves * kDecodeJB) {
+    uint4 wv[kDecodeJB];
+    uint32_t sv[kDecodeJB];
+    bf16x8_t xv[kDecodeJB][4];
+    // groups past K, columns past N and token rows past M read as zero
+#pragma unroll
+    for (int b = 0; b < kDecodeJB; ++b) {
+      const int j = j0 + kGemvWaves * b;
+      if (j < J && col_ok) {
+        wv[b] = *reinterpret_cast<const uint4*>(wrow + 64 * (int64_t)j);
+        sv[b] = *reinterpret_cast<const uint16_t*>(srow + 8 * (int64_t)j);
+      } else {
+        wv[b] = make_uint4(0u, 0u, 0u, 0u);
+        sv[b] = 0u;
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        if (j < J && row_ok)
+          xv[b][t] = *reinterpret_cast<const bf16x8_t*>(xrow + 128 * (int64_t)j + 8 * t);
+        else
+          xv[b][t] = bf16x8_t{};
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < kDecodeJB; ++b) {
+      const int j = j0 + kGemvWaves * b;
+      if (j < J) {  // wave-uniform
+        const float s0 = decode_e4m3<0>(sv[b]), s1 = decode_e4m3<1>(sv[b]);
+        const uint32_t pw[4] = {wv[b].x, wv[b].y, wv[b].z, wv[b].w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv[b][t], dequant8(pw[t], t < 2 ? s0 : s1),
+                                                        acc, 0, 0, 0);
+      }
+    }
+  }
+  // lane l holds rows 4 (l / 16) .. + 3 of column l % 16
+  red[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+    f32x4_t sum = red[0][lane];
+#pragma unroll
+    for (int w = 1; w < kGemvWaves; ++w) sum += red[w][lane];
+    const float gv = p.g[0];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * g + i;
+      if (m < M && col_ok) {
+        const float v = gv * sum[i];
+        const int64_t o = (int64_t)m * N + n;
+        if (p.out_f32)
+          static_cast<float*>(p.y)[o] = v;
+        else
+          static_cast<uint16_t*>(p.y)[o] = (uint16_t)float_to_bf16_rne(v);
+      }
+    }
+  }
+}
+
 hipError_t launch_gemv(const GemmPlan& pl, const GemmParams& p, hipStream_t stream) {
+  if (pl.kind == 7) {
+    hipLaunchKernelGGL(decode_mfma_kernel, dim3((unsigned)pl.grid), dim3(kGemvThreads), 0, stream,
+                       p);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)pl.grid), block(kGemvThreads);
   switch (pl.bm) {
     case 1: hipLaunchKernelGGL(gemv_kernel<1>, grid, block, pl.dyn_lds, stream, p); break;

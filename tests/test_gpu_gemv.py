@@ -1,11 +1,13 @@
-"""GPU parity of the dot-product kernel for dense products of one to four rows.
+"""GPU parity of the decode kernels for dense products of one to sixteen rows.
 
 Decode products ("The FP4 Frontier", Finding 7: bandwidth-bound at small
 batch) with at most four token rows run on a kernel that keeps the block
 scale out of the inner loop: per 16-element block the exact E2M1 values are
 dotted with the activations in FP32, and the block's E4M3 scale multiplies
-that partial sum.  Same tolerances as every GEMM: FP32 output within 1e-5,
-BF16 within 4e-3 of sum_k |x * w|."""
+that partial sum.  Five to sixteen rows (k % 128 == 0) run on one MFMA row
+tile per 16 columns with whole K per workgroup and a permuted K order inside
+each MFMA.  Same tolerances as every GEMM: FP32 output within 1e-5, BF16
+within 4e-3 of sum_k |x * w|."""
 import os
 
 import numpy as np
@@ -74,14 +76,36 @@ def test_against_oracle(m, n, k):
     check_close(run_gemm(nv, x, qw, torch.bfloat16), y_ref, d, "bf16 %dx%dx%d" % (m, n, k))
 
 
+SHAPES_128 = [
+    (1, 128),      # one 128-deep K group: seven of the eight waves idle
+    (17, 384),     # ragged column tile
+    (300, 1152),   # K groups not a multiple of the eight waves
+    (64, 16384),   # a wave's second batch of K groups
+]
+
+
+@pytest.mark.parametrize("m", [5, 8, 13, 16])
+@pytest.mark.parametrize("n,k", SHAPES_128)
+def test_mfma_rows_against_oracle(m, n, k):
+    nv = require_gpu()
+    key = m * 1000003 + n * 1009 + k
+    w = W.normal_bf16((n, k), 0.05, (83, key, 0))
+    x = W.normal_bf16((m, k), 1.0, (83, key, 1))
+    p, s, g = oracle_weight(w)
+    y_ref, d = oracle.gemm(x, p, s, g[0])
+    qw = to_qw(nv, p, s, g)
+    check_close(run_gemm(nv, x, qw, torch.float32), y_ref, d, "f32 %dx%dx%d" % (m, n, k))
+    check_close(run_gemm(nv, x, qw, torch.bfloat16), y_ref, d, "bf16 %dx%dx%d" % (m, n, k))
+
+
 @pytest.fixture(scope="module")
 def decode_weight():
     return oracle_weight(W.decode_weight())
 
 
-@pytest.mark.parametrize("m", [1, 4])
+@pytest.mark.parametrize("m", [1, 4, 5, 16])
 def test_decode_weight_both_paths(decode_weight, m):
-    """N = 4096, K = 7168 with 0.1 % outliers: the dot-product kernel and the
+    """N = 4096, K = 7168 with 0.1 % outliers: the decode kernel and the
     K-phase kernel (override NVFP4_GEMV=0) both within tolerance; the former
     reproducible bit for bit."""
     nv = require_gpu()

@@ -169,8 +169,10 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemmParams p) {
 // K -- slot 8 g + i of step t is K = 128 j + 32 g + 8 t + i -- applied to both
 // operands alike, so the product is unchanged.  Partial tiles of the 8 waves
 // are summed in wave order through LDS.
-constexpr int kDecodeJB = 8;  // 128-deep K groups a lane loads before it multiplies them
-
+// JB: 128-deep K groups a lane loads before it multiplies them (1 to 8; the
+// launch picks the smallest count that covers a wave's groups in one pass
+// when it can).
+template <int JB>
 __global__ __launch_bounds__(kGemvThreads) void decode_mfma_kernel(GemmParams p) {
   __shared__ f32x4_t red[kGemvWaves][kWave];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -184,31 +186,26 @@ __global__ __launch_bounds__(kGemvThreads) void decode_mfma_kernel(GemmParams p)
   const uint8_t* srow = p.s + (int64_t)(col_ok ? n : 0) * (K / 16) + 2 * g;
   const uint16_t* xrow = p.x + (int64_t)(row_ok ? c16 : 0) * K + 32 * g;
   f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int j0 = wave; j0 < J; j0 += kGemvWaves * kDecodeJB) {
-    uint4 wv[kDecodeJB];
-    uint32_t sv[kDecodeJB];
-    bf16x8_t xv[kDecodeJB][4];
-    // groups past K, columns past N and token rows past M read as zero
+  for (int j0 = wave; j0 < J; j0 += kGemvWaves * JB) {
+    uint4 wv[JB];
+    uint32_t sv[JB];
+    bf16x8_t xv[JB][4];
+    // unconditional loads, so that no branch separates them and each group
+    // is multiplied as soon as its own loads have landed: a group past K
+    // re-reads the last group (and is not multiplied), a column past N reads
+    // weight row 0 and a token row past M reads token row 0 (their outputs
+    // are not stored)
 #pragma unroll
-    for (int b = 0; b < kDecodeJB; ++b) {
-      const int j = j0 + kGemvWaves * b;
-      if (j < J && col_ok) {
-        wv[b] = *reinterpret_cast<const uint4*>(wrow + 64 * (int64_t)j);
-        sv[b] = *reinterpret_cast<const uint16_t*>(srow + 8 * (int64_t)j);
-      } else {
-        wv[b] = make_uint4(0u, 0u, 0u, 0u);
-        sv[b] = 0u;
-      }
+    for (int b = 0; b < JB; ++b) {
+      const int j = min(j0 + kGemvWaves * b, J - 1);
+      wv[b] = *reinterpret_cast<const uint4*>(wrow + 64 * (int64_t)j);
+      sv[b] = *reinterpret_cast<const uint16_t*>(srow + 8 * (int64_t)j);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        if (j < J && row_ok)
-          xv[b][t] = *reinterpret_cast<const bf16x8_t*>(xrow + 128 * (int64_t)j + 8 * t);
-        else
-          xv[b][t] = bf16x8_t{};
-      }
+      for (int t = 0; t < 4; ++t)
+        xv[b][t] = *reinterpret_cast<const bf16x8_t*>(xrow + 128 * (int64_t)j + 8 * t);
     }
 #pragma unroll
-    for (int b = 0; b < kDecodeJB; ++b) {
+    for (int b = 0; b < JB; ++b) {
       const int j = j0 + kGemvWaves * b;
       if (j < J) {  // wave-uniform
         const float s0 = decode_e4m3<0>(sv[b]), s1 = decode_e4m3<1>(sv[b]);
@@ -245,8 +242,18 @@ __global__ __launch_bounds__(kGemvThreads) void decode_mfma_kernel(GemmParams p)
 
 hipError_t launch_gemv(const GemmPlan& pl, const GemmParams& p, hipStream_t stream) {
   if (pl.kind == 7) {
-    hipLaunchKernelGGL(decode_mfma_kernel, dim3((unsigned)pl.grid), dim3(kGemvThreads), 0, stream,
-                       p);
+    const dim3 grid((unsigned)pl.grid), block(kGemvThreads);
+    const int per_wave = (p.k / 128 + kGemvWaves - 1) / kGemvWaves;  // K groups per wave
+    switch (per_wave < 8 ? per_wave : 8) {
+      case 1: hipLaunchKernelGGL(decode_mfma_kernel<1>, grid, block, 0, stream, p); break;
+      case 2: hipLaunchKernelGGL(decode_mfma_kernel<2>, grid, block, 0, stream, p); break;
+      case 3: hipLaunchKernelGGL(decode_mfma_kernel<3>, grid, block, 0, stream, p); break;
+      case 4: hipLaunchKernelGGL(decode_mfma_kernel<4>, grid, block, 0, stream, p); break;
+      case 5: hipLaunchKernelGGL(decode_mfma_kernel<5>, grid, block, 0, stream, p); break;
+      case 6: hipLaunchKernelGGL(decode_mfma_kernel<6>, grid, block, 0, stream, p); break;
+      case 7: hipLaunchKernelGGL(decode_mfma_kernel<7>, grid, block, 0, stream, p); break;
+      default: hipLaunchKernelGGL(decode_mfma_kernel<8>, grid, block, 0, stream, p); break;
+    }
     return hipGetLastError();
   }
   const dim3 grid((unsigned)pl.grid), block(kGemvThreads);

@@ -111,22 +111,37 @@ __device__ __forceinline__ void encode_block(u32x4_t v0, u32x4_t v1, float g, ui
   const bool fast = d >= 0x1p-98f && d <= 0x1p100f;
   const float r = fast ? 1.0f / d : 0.0f;
 
+  // Each pair of elements: the FP32 quotients |w| / d (Markstein or IEEE
+  // division, as above; 0 when d == 0) take the sign of w, and gfx950's
+  // FP32 -> E2M1 pack conversion (scale operand 1.0) rounds them to nearest,
+  // ties to even, saturating at 6 and keeping the sign of a zero: exactly
+  // sign | encode_e2m1_mag(|q|) -- a GPU probe compared the two on every
+  // finite non-negative FP32 pattern, +inf and their negatives, with no
+  // difference.  Element 2j goes to the low nibble of byte j.
   uint32_t words[2] = {0u, 0u};
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
+  for (int e = 0; e < 16; e += 2) {
     const uint32_t dw = (e < 8) ? v0[e / 2] : v1[(e - 8) / 2];
-    const uint32_t h = (e & 1) ? (dw >> 16) : (dw & 0xFFFFu);
-    const float x = bf16_bits_to_float(h & 0x7FFFu);
-    uint32_t mag = 0;
-    if (fast) {
-      const float q0 = x * r;
-      const float q = __builtin_fmaf(__builtin_fmaf(-q0, d, x), r, q0);
-      mag = encode_e2m1_mag(q);
-    } else if (d != 0.0f) {
-      mag = encode_e2m1_mag(x / d);
+    const float xs[2] = {__uint_as_float(dw << 16), __uint_as_float(dw & 0xFFFF0000u)};
+    float q[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const float x = __builtin_fabsf(xs[i]);
+      float qi = 0.0f;
+      if (fast) {
+        const float q0 = x * r;
+        qi = __builtin_fmaf(__builtin_fmaf(-q0, d, x), r, q0);
+      } else if (d != 0.0f) {
+        qi = x / d;
+      }
+      q[i] = __builtin_copysignf(qi, xs[i]);
     }
-    const uint32_t code = ((h >> 15) << 3) | mag;
-    words[e / 8] |= code << (4 * (e % 8));
+    switch ((e % 8) / 2) {
+      case 0: words[e / 8] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(words[e / 8], q[0], q[1], 1.0f, 0); break;
+      case 1: words[e / 8] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(words[e / 8], q[0], q[1], 1.0f, 1); break;
+      case 2: words[e / 8] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(words[e / 8], q[0], q[1], 1.0f, 2); break;
+      default: words[e / 8] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(words[e / 8], q[0], q[1], 1.0f, 3); break;
+    }
   }
   u32x2_t outw = {words[0], words[1]};
   *reinterpret_cast<u32x2_t*>(packed8) = outw;

@@ -347,3 +347,50 @@ def moe_combine(y, token_rows, weights):
             out[t] += weights[t, j] * y[r]
             d[t] += np.abs(weights[t, j] * y[r])
     return out, d
+
+
+# ---- W4A4: both operands in NVFP4 -------------------------------------------
+#
+# The pages' FP4 GEMMs with block-scaled FP4 data and scale tiles for both
+# operands ("The SM120 FP4 GEMM Kernel Investigation", section "The
+# Comprehensive Synthesis: Message 6"; "The Tile That Didn't Fit: Diagnosing
+# FP4 Kernel Underutilization on Blackwell SM120", section "Why Tile Size
+# Matters for FP4 Performance").  Activations take the same encoding as the
+# weights (two tiers, one E4M3 scale per 16 values along K, one FP32 scale
+# per tensor), so the product is the plain definition over the two decoded
+# operands: y = g_x * g_w * sum_k x_dec[m, k] * w_dec[n, k], in FP64.
+
+def gemm_w4a4(x_packed, x_scales, g_x, packed, scales, g):
+    """(y, D) float64 [m, n]: y = g_x * g * x_dec @ w_dec^T and
+    D = |g_x * g| * |x_dec| @ |w_dec|^T, x_dec / w_dec the decoded operands
+    without their global scales."""
+    xd = dequant(x_packed, x_scales)
+    wd = dequant(packed, scales)
+    if xd.shape[1] != wd.shape[1]:
+        raise ValueError("k mismatch")
+    sg = float(np.float32(np.asarray(g_x).reshape(-1)[0])) * float(
+        np.float32(np.asarray(g).reshape(-1)[0]))
+    y = sg * (xd @ wd.T)
+    d = abs(sg) * (np.abs(xd) @ np.abs(wd).T)
+    return y, d
+
+
+def grouped_gemm_w4a4(x_packed, x_scales, g_x, offsets, packed, scales, g):
+    """Rows [offsets[e], offsets[e+1]) of the NVFP4 activations (one global
+    scale g_x for all rows) times expert e's weight with g[e].  Rows of empty
+    segments stay NaN."""
+    x_packed = _c(x_packed, np.uint8)
+    x_scales = _c(x_scales, np.uint8)
+    offsets = _c(offsets, np.int64)
+    g = _c(g, np.float32)
+    rows = x_packed.shape[0]
+    E, n, _ = np.asarray(packed).shape
+    y = np.full((rows, n), np.nan, np.float64)
+    d = np.full((rows, n), np.nan, np.float64)
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if b > a:
+            y[a:b], d[a:b] = gemm_w4a4(x_packed[a:b], x_scales[a:b], g_x, packed[e], scales[e],
+                                       g[e])
+    return y, d
+

@@ -33,7 +33,9 @@ MAX_EXPERTS = 1024
 
 EXPORTED = [
     "nvfp4_quantize", "nvfp4_gemm", "nvfp4_grouped_gemm", "nvfp4_grouped_gemm_swiglu",
-    "nvfp4_grouped_gemm_gather", "nvfp4_moe_combine",
+    "nvfp4_grouped_gemm_gather", "nvfp4_moe_combine", "nvfp4_gemm_w4a4",
+    "nvfp4_grouped_gemm_w4a4", "nvfp4_gemm_w4a4_workspace_size",
+    "nvfp4_grouped_gemm_w4a4_workspace_size",
     "nvfp4_quantize_workspace_size",
     "nvfp4_gemm_workspace_size", "nvfp4_grouped_gemm_workspace_size",
     "nvfp4_workspace_counter_bytes", "nvfp4_workspace_init", "nvfp4_status_string",
@@ -76,6 +78,15 @@ def load_library(path: str = LIB_PATH):
         lib.nvfp4_grouped_gemm_gather.restype = I32
         lib.nvfp4_moe_combine.argtypes = [P, I32, I64, P, P, I64, I64, I64, P, I32, P, P]
         lib.nvfp4_moe_combine.restype = I32
+        lib.nvfp4_gemm_w4a4.argtypes = [P, P, P, I64, I64, I64, P, P, P, P, I32, P, SZ, P]
+        lib.nvfp4_gemm_w4a4.restype = I32
+        lib.nvfp4_grouped_gemm_w4a4.argtypes = [P, P, P, I64, P, I64, I64, I64, P, P, P, P, I32,
+                                                P, P, SZ, P]
+        lib.nvfp4_grouped_gemm_w4a4.restype = I32
+        lib.nvfp4_gemm_w4a4_workspace_size.argtypes = [I64, I64, I64]
+        lib.nvfp4_gemm_w4a4_workspace_size.restype = SZ
+        lib.nvfp4_grouped_gemm_w4a4_workspace_size.argtypes = [I64, I64, I64, I64]
+        lib.nvfp4_grouped_gemm_w4a4_workspace_size.restype = SZ
         lib.nvfp4_quantize_workspace_size.argtypes = [I64, I64, I64]
         lib.nvfp4_quantize_workspace_size.restype = SZ
         lib.nvfp4_gemm_workspace_size.argtypes = [I64, I64, I64]
@@ -167,6 +178,30 @@ def nvfp4_gemm_workspace_size(m, n, k) -> int:
 
 def nvfp4_grouped_gemm_workspace_size(rows, num_experts, n, k) -> int:
     return load_library().nvfp4_grouped_gemm_workspace_size(rows, num_experts, n, k)
+
+
+def nvfp4_gemm_w4a4_workspace_size(m, n, k) -> int:
+    return load_library().nvfp4_gemm_w4a4_workspace_size(m, n, k)
+
+
+def nvfp4_grouped_gemm_w4a4_workspace_size(rows, num_experts, n, k) -> int:
+    return load_library().nvfp4_grouped_gemm_w4a4_workspace_size(rows, num_experts, n, k)
+
+
+def nvfp4_gemm_w4a4(x_packed, x_scales, x_g, m, n, k, packed, scales, global_scale, y, out,
+                    workspace, ws_bytes, stream=None):
+    return load_library().nvfp4_gemm_w4a4(
+        _ptr(x_packed), _ptr(x_scales), _ptr(x_g), m, n, k, _ptr(packed), _ptr(scales),
+        _ptr(global_scale), _ptr(y), out, _ptr(workspace), ws_bytes, _stream(stream))
+
+
+def nvfp4_grouped_gemm_w4a4(x_packed, x_scales, x_g, rows, offsets, num_experts, n, k, packed,
+                            scales, global_scales, y, out, d_status, workspace, ws_bytes,
+                            stream=None):
+    return load_library().nvfp4_grouped_gemm_w4a4(
+        _ptr(x_packed), _ptr(x_scales), _ptr(x_g), rows, _ptr(offsets), num_experts, n, k,
+        _ptr(packed), _ptr(scales), _ptr(global_scales), _ptr(y), out, _ptr(d_status),
+        _ptr(workspace), ws_bytes, _stream(stream))
 
 
 def nvfp4_workspace_counter_bytes() -> int:
@@ -373,3 +408,44 @@ def moe_combine(y: torch.Tensor, token_rows: torch.Tensor, weights: torch.Tensor
                              OUT_F32 if out.dtype == torch.float32 else OUT_BF16, d_status,
                              stream), "nvfp4_moe_combine")
     return out
+
+
+def gemm_w4a4(xq: QuantizedWeight, qw: QuantizedWeight, out_dtype=torch.bfloat16,
+              out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """y [m, n] = g_x g_w x_dec @ w_dec^T for activations in NVFP4 (xq, e.g.
+    from quantize(x) of a [m, k] BF16 tensor) and an NVFP4 weight."""
+    if xq.packed.dim() != 2 or qw.packed.dim() != 2 or xq.k != qw.k:
+        raise ValueError("activations [m, k/2] and weight [n, k/2] with the same k")
+    m, k, n = xq.packed.shape[0], xq.k, qw.n
+    code = OUT_F32 if out_dtype == torch.float32 else OUT_BF16
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=xq.packed.device)
+    nbytes = nvfp4_gemm_w4a4_workspace_size(m, n, k)
+    ws = _gemm_ws.get(nbytes, xq.packed.device, stream)
+    _check(nvfp4_gemm_w4a4(xq.packed, xq.scales, xq.global_scale, m, n, k, qw.packed, qw.scales,
+                           qw.global_scale, out, code, ws, nbytes, stream), "nvfp4_gemm_w4a4")
+    return out
+
+
+def grouped_gemm_w4a4(xq: QuantizedWeight, offsets: torch.Tensor, qw: QuantizedWeight,
+                      out_dtype=torch.bfloat16, out: torch.Tensor | None = None,
+                      d_status: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Rows [offsets[e], offsets[e+1]) of the NVFP4 activations (one global
+    scale for all rows) times expert e's NVFP4 weight."""
+    if xq.packed.dim() != 2 or qw.packed.dim() != 3 or xq.k != qw.k:
+        raise ValueError("activations [rows, k/2] and weight [E, n, k/2] with the same k")
+    rows, k = xq.packed.shape[0], xq.k
+    E, n, _ = qw.packed.shape
+    if offsets.dtype != torch.int32 or offsets.numel() != E + 1 or not offsets.is_cuda:
+        raise ValueError("offsets must be a device int32 tensor of E+1 entries")
+    code = OUT_F32 if out_dtype == torch.float32 else OUT_BF16
+    if out is None:
+        out = torch.empty((rows, n), dtype=out_dtype, device=xq.packed.device)
+    nbytes = nvfp4_grouped_gemm_w4a4_workspace_size(rows, E, n, k)
+    ws = _gemm_ws.get(nbytes, xq.packed.device, stream)
+    _check(nvfp4_grouped_gemm_w4a4(xq.packed, xq.scales, xq.global_scale, rows,
+                                   offsets.contiguous(), E, n, k, qw.packed, qw.scales,
+                                   qw.global_scale, out, code, d_status, ws, nbytes, stream),
+           "nvfp4_grouped_gemm_w4a4")
+    return out
+

@@ -11,7 +11,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libnvfp4.so")
-SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "gemv.hip", "combine.hip"]
+SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "gemv.hip", "combine.hip", "w4a4.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -225,6 +225,91 @@ nvfp4_status_t nvfp4_grouped_gemm_swiglu(const void* x_bf16, int64_t rows,
                   reinterpret_cast<hipStream_t>(stream), true, 1);
 }
 
+// ---- W4A4 -----------------------------------------------------------------
+
+namespace {
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+// Workspace of a W4A4 call: the GEMM's own workspace first (split-K counters
+// must sit at its start), then the decoded BF16 activations, then the
+// per-expert products of the global scales.  The counter region is reserved
+// even when this call does not split K: a workspace serves calls of every
+// shape, and the counters must stay zero between them.
+struct W4A4Layout {
+  size_t gemm, x_off, g_off, total;
+};
+W4A4Layout w4a4_layout(int64_t rows, int64_t E, int64_t n, int64_t k, bool grouped) {
+  W4A4Layout l;
+  l.gemm = nvfp4::plan_gemm(rows, E, n, k, grouped, cu_count()).ws_bytes;
+  l.x_off = align256(std::max(l.gemm, nvfp4::kCounterBytes));
+  l.g_off = l.x_off + align256((size_t)rows * (size_t)k * 2);
+  l.total = l.g_off + align256((size_t)E * 4);
+  return l;
+}
+}  // namespace
+
+size_t nvfp4_gemm_w4a4_workspace_size(int64_t m, int64_t n, int64_t k) {
+  if (m <= 0 || n <= 0 || check_k(k) != NVFP4_OK) return 0;
+  return w4a4_layout(m, 1, n, k, false).total;
+}
+
+size_t nvfp4_grouped_gemm_w4a4_workspace_size(int64_t rows, int64_t num_experts, int64_t n,
+                                              int64_t k) {
+  if (rows <= 0 || num_experts <= 0 || n <= 0 || check_k(k) != NVFP4_OK) return 0;
+  return w4a4_layout(rows, num_experts, n, k, true).total;
+}
+
+static nvfp4_status_t run_w4a4(const uint8_t* x_packed, const uint8_t* x_scales, const float* x_g,
+                               int64_t rows, const int32_t* offsets, int64_t E, int64_t n,
+                               int64_t k, const uint8_t* packed, const uint8_t* scales,
+                               const float* g, void* y, nvfp4_out_t out, uint32_t* d_status,
+                               void* workspace, size_t ws_bytes, hipStream_t stream,
+                               bool grouped) {
+  if (!x_scales || !x_g) return NVFP4_ERR_INVALID_ARGUMENT;
+  if ((reinterpret_cast<uintptr_t>(x_g) & 3u) != 0) return NVFP4_ERR_MISALIGNED;
+  const W4A4Layout l = w4a4_layout(rows, E, n, k, grouped);
+  if (workspace == nullptr || ws_bytes < l.total) return NVFP4_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return NVFP4_ERR_MISALIGNED;
+  char* ws = static_cast<char*>(workspace);
+  uint16_t* x_bf16 = reinterpret_cast<uint16_t*>(ws + l.x_off);
+  float* g_comb = reinterpret_cast<float*>(ws + l.g_off);
+  hipError_t err = nvfp4::launch_dequant_rows(x_packed, x_scales, rows, k, x_bf16, x_g, g,
+                                              g_comb, (int)E, stream);
+  if (err != hipSuccess) return hip_status(err);
+  return run_gemm(x_bf16, rows, offsets, E, n, k, packed, scales, g_comb, y, out, d_status, ws,
+                  l.gemm, stream, grouped);
+}
+
+nvfp4_status_t nvfp4_gemm_w4a4(const uint8_t* x_packed, const uint8_t* x_scales,
+                               const float* x_global_scale, int64_t m, int64_t n, int64_t k,
+                               const uint8_t* packed, const uint8_t* scales,
+                               const float* global_scale, void* y, nvfp4_out_t out,
+                               void* workspace, size_t ws_bytes, void* stream) {
+  nvfp4_status_t st = check_gemm_common(x_packed, m, n, k, packed, scales, global_scale, y, out);
+  if (st != NVFP4_OK || m == 0) return st;
+  return run_w4a4(x_packed, x_scales, x_global_scale, m, nullptr, 1, n, k, packed, scales,
+                  global_scale, y, out, nullptr, workspace, ws_bytes,
+                  reinterpret_cast<hipStream_t>(stream), false);
+}
+
+nvfp4_status_t nvfp4_grouped_gemm_w4a4(const uint8_t* x_packed, const uint8_t* x_scales,
+                                       const float* x_global_scale, int64_t rows,
+                                       const int32_t* expert_offsets, int64_t num_experts,
+                                       int64_t n, int64_t k, const uint8_t* packed,
+                                       const uint8_t* scales, const float* global_scales,
+                                       void* y, nvfp4_out_t out, uint32_t* d_status,
+                                       void* workspace, size_t ws_bytes, void* stream) {
+  if (num_experts < 1) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (num_experts > NVFP4_MAX_EXPERTS) return NVFP4_ERR_UNSUPPORTED;
+  nvfp4_status_t st =
+      check_gemm_common(x_packed, rows, n, k, packed, scales, global_scales, y, out);
+  if (st != NVFP4_OK || rows == 0) return st;
+  if (!expert_offsets) return NVFP4_ERR_INVALID_ARGUMENT;
+  if ((reinterpret_cast<uintptr_t>(expert_offsets) & 3u) != 0) return NVFP4_ERR_MISALIGNED;
+  return run_w4a4(x_packed, x_scales, x_global_scale, rows, expert_offsets, num_experts, n, k,
+                  packed, scales, global_scales, y, out, d_status, workspace, ws_bytes,
+                  reinterpret_cast<hipStream_t>(stream), true);
+}
+
 nvfp4_status_t nvfp4_moe_combine(const void* y, nvfp4_out_t y_type, int64_t rows,
                                  const int32_t* token_rows, const float* weights,
                                  int64_t tokens, int64_t topk, int64_t n, void* out,

@@ -74,6 +74,11 @@ hipError_t launch_gemv(const GemmPlan& plan, const GemmParams& p, hipStream_t st
 bool plan_pairs_tiles(const GemmPlan& plan);
 hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t stream);
 
+// ---- W4A4: decode NVFP4 activations to BF16, form g_w[e] * g_x ----------------
+hipError_t launch_dequant_rows(const uint8_t* packed, const uint8_t* scales, int64_t rows,
+                               int64_t k, uint16_t* x_bf16, const float* g_x, const float* g_w,
+                               float* g_out, int num_experts, hipStream_t stream);
+
 // ---- MoE combine -----------------------------------------------------------
 hipError_t launch_moe_combine(const void* y, bool y_f32, int64_t rows, const int32_t* token_rows,
                               const float* w, int64_t tokens, int topk, int n, void* out,

@@ -201,6 +201,40 @@ nvfp4_status_t nvfp4_moe_combine(const void* y, nvfp4_out_t y_type, int64_t rows
                                  int64_t tokens, int64_t topk, int64_t n, void* out,
                                  nvfp4_out_t out_type, uint32_t* d_status, void* stream);
 
+/* W4A4: the activations are NVFP4 too, in the weights' encoding (block-scaled
+ * FP4 data and scales for both operands: "The SM120 FP4 GEMM Kernel
+ * Investigation", section "The Comprehensive Synthesis: Message 6").
+ * x_packed [rows][k/2] and x_scales [rows][k/16] as written by nvfp4_quantize
+ * for the activation tensor, x_global_scale one device float (its g).
+ * y = x_global_scale * g[e] * x_dec . w_dec^T over each expert's rows, FP32
+ * accumulation, x_dec / w_dec the decoded operands without their global
+ * scales.  The activations are decoded once per call into the workspace
+ * (BF16, exact), then the W4A16 kernels run on them with the global scale
+ * product fl32(g[e] * x_global_scale); the workspace therefore always has a
+ * nonzero size (nvfp4_*_w4a4_workspace_size) and must be initialised once
+ * with nvfp4_workspace_init like the GEMM workspaces.  Its first
+ * nvfp4_workspace_counter_bytes() bytes are the split-K counters and are
+ * never used for the activations, so one workspace can serve W4A16 and W4A4
+ * calls of any shape.  Same argument rules,
+ * alignment and status behaviour as nvfp4_gemm / nvfp4_grouped_gemm
+ * (x_packed takes the place of x_bf16); x_scales and x_global_scale must be
+ * non-null, x_global_scale 4-byte aligned. */
+nvfp4_status_t nvfp4_gemm_w4a4(const uint8_t* x_packed, const uint8_t* x_scales,
+                               const float* x_global_scale, int64_t m, int64_t n, int64_t k,
+                               const uint8_t* packed, const uint8_t* scales,
+                               const float* global_scale, void* y, nvfp4_out_t out,
+                               void* workspace, size_t ws_bytes, void* stream);
+nvfp4_status_t nvfp4_grouped_gemm_w4a4(const uint8_t* x_packed, const uint8_t* x_scales,
+                                       const float* x_global_scale, int64_t rows,
+                                       const int32_t* expert_offsets, int64_t num_experts,
+                                       int64_t n, int64_t k, const uint8_t* packed,
+                                       const uint8_t* scales, const float* global_scales,
+                                       void* y, nvfp4_out_t out, uint32_t* d_status,
+                                       void* workspace, size_t ws_bytes, void* stream);
+size_t nvfp4_gemm_w4a4_workspace_size(int64_t m, int64_t n, int64_t k);
+size_t nvfp4_grouped_gemm_w4a4_workspace_size(int64_t rows, int64_t num_experts, int64_t n,
+                                              int64_t k);
+
 /* Workspace sizes (bytes) for the calls above; 0 means none is needed.  The
  * sizes depend on the current device's compute-unit count. */
 size_t nvfp4_quantize_workspace_size(int64_t batch, int64_t n, int64_t k);

@@ -149,6 +149,24 @@ def test_moe_combine_host_validation(lib):
     assert call(tokens=0, y=None, tr=None, w=None, out=None) == 0
 
 
+def test_w4a4_host_validation(lib):
+    def call(xs=A, xg=A, m=4, ws=None, nbytes=0):
+        return nv.nvfp4_gemm_w4a4(A, xs, xg, m, 64, 32, A, A, A, A, nv.OUT_BF16, ws, nbytes, S)
+    assert call(xs=None) == 1
+    assert call(xg=FakePtr(0x10002)) == 2
+    assert call() == 4                      # the decoded activations need a workspace
+    assert nv.nvfp4_gemm_w4a4_workspace_size(4, 64, 32) >= 4 * 32 * 2
+    assert call(m=0, xs=None, xg=None) == 0
+
+    def gcall(E=4, off=A, rows=8):
+        return nv.nvfp4_grouped_gemm_w4a4(A, A, A, rows, off, E, 64, 32, A, A, A, A,
+                                          nv.OUT_BF16, None, None, 0, S)
+    assert gcall(off=None) == 1
+    assert gcall(E=nv.MAX_EXPERTS + 1) == 3
+    assert gcall() == 4
+    assert gcall(rows=0, off=None) == 0
+
+
 def test_quantize_host_validation(lib):
     def call(batch=1, n=4, k=32, w=A, ws=None):
         return nv.nvfp4_quantize(w, batch, n, k, A, A, A, None, ws, 0, S)

@@ -390,6 +390,29 @@ def combine_extras(launches):
     return out
 
 
+def w4a4_extras(launches):
+    """The ~16 tok/expert up launch with NVFP4 activations: quantizing the
+    activations, then the W4A4 launch (decode of the activations included),
+    against the W4A16 launch on the same shape."""
+    import torch
+    import block_scaled_fp4_nibble_amd as nv
+
+    out = {}
+    for L in launches:
+        if L["name"] != "up_uniform_16tpe":
+            continue
+        xq = nv.quantize(L["x"])
+        ms_q = ms_4 = ms_16 = float("inf")
+        for _ in range(2):
+            ms_q = min(ms_q, time_fn(lambda: nv.quantize(L["x"]), 20, 3))
+            ms_4 = min(ms_4, time_fn(lambda: nv.grouped_gemm_w4a4(xq, L["off"], L["qw"],
+                                                                   out=L["y"]), 20, 3))
+            ms_16 = min(ms_16, time_fn(lambda: run_launch(L), 20, 3))
+        out["w4a4_" + L["name"]] = {"us": ms_4 * 1e3, "w4a16_us": ms_16 * 1e3,
+                                     "quantize_activations_us": ms_q * 1e3}
+    return out
+
+
 def dense_only(m, n, k):
     """One dense GEMM shape: 10 warm-up and 20 timed launches."""
     import torch
@@ -568,6 +591,7 @@ def main():
         ex = swiglu_extras(launches)
         ex.update(gather_extras(launches))
         ex.update(combine_extras(launches))
+        ex.update(w4a4_extras(launches))
         ex.update(extras())
         result["extras"] = ex
     if not args.no_cpu_baseline:

@@ -44,17 +44,6 @@ __device__ __forceinline__ uint32_t encode_e4m3(float x) {
   return code > 0x7Eu ? 0x7Eu : code;
 }
 
-// E2M1 magnitude code (0..7) of a non-negative float (may be +inf).
-// q >= 6 saturates; below 1 the code is rint(2q) (0, 0.5, 1.0); otherwise the
-// float's mantissa is rounded to one bit and the exponent rebiased to 1.
-__device__ __forceinline__ uint32_t encode_e2m1_mag(float q) {
-  if (q >= kE2M1Max) return 7u;
-  if (q < 1.0f) return (uint32_t)__builtin_rintf(q * 2.0f);
-  uint32_t u = __float_as_uint(q);
-  uint32_t r = (u + 0x1FFFFFu + ((u >> 22) & 1u)) >> 22;  // exponent | 1 mantissa bit
-  return r - ((127u - 1u) << 1);
-}
-
 // ---- decoders ---------------------------------------------------------------
 
 // E4M3 byte `sel` (0..3) of a dword to float (gfx950 converts OCP E4M3FN).

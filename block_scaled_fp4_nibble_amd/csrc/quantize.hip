@@ -115,11 +115,13 @@ __device__ __forceinline__ void encode_block(u32x4_t v0, u32x4_t v1, float g, ui
 
   // Each pair of elements: the FP32 quotients |w| / d (Markstein or IEEE
   // division, as above; 0 when d == 0) take the sign of w, and gfx950's
-  // FP32 -> E2M1 pack conversion (scale operand 1.0) rounds them to nearest,
-  // ties to even, saturating at 6 and keeping the sign of a zero: exactly
-  // sign | encode_e2m1_mag(|q|) -- a GPU probe compared the two on every
-  // finite non-negative FP32 pattern, +inf and their negatives, with no
-  // difference.  Element 2j goes to the low nibble of byte j.
+  // FP32 -> E2M1 pack conversion (scale operand 1.0) turns them into codes:
+  // the sign bit, then the nearest E2M1 magnitude with ties to the even code
+  // (0.25 -> 0, 0.75 -> 1, 1.25 -> 1, 1.75 -> 2, 2.5 -> 2, 3.5 -> 4, 5 -> 4),
+  // saturating at 6, with the sign kept on a zero magnitude.  A GPU probe
+  // compared it with a bit-manipulation encoder of that rule on every finite
+  // non-negative FP32 pattern, +inf and their negatives: no difference.
+  // Element 2j goes to the low nibble of byte j.
   uint32_t words[2] = {0u, 0u};
 #pragma unroll
   for (int e = 0; e < 16; e += 2) {

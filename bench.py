@@ -593,6 +593,15 @@ def main():
         ex.update(combine_extras(launches))
         ex.update(w4a4_extras(launches))
         ex.update(extras())
+        # the same rates against what this box measured (context for the
+        # spec peaks): the dominant kernel's algorithmic GB/s over a device
+        # copy's, the 8192^3 NVFP4 GEMM over hipBLASLt's BF16 GEMM
+        ex["vs_measured_ceilings"] = {
+            "roofline_kernel_frac_of_copy_GBps":
+                achieved / ex["measured_copy_1GiB"]["GBps"],
+            "dense_8192_cubed_frac_of_hipblaslt_bf16":
+                ex["dense_8192_cubed"]["TFLOPS"] / ex["measured_bf16_gemm_8192_cubed"]["TFLOPS"],
+        }
         result["extras"] = ex
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

@@ -128,13 +128,31 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total)
   return base + incl - v;
 }
 
-// Per-workgroup schedule: the exclusive prefix of work units per expert lives
-// in dynamic LDS (4 (E + 1) bytes, sized at launch); the expert segments
-// themselves are read from the offsets in device memory.
+// Per-workgroup schedule in dynamic LDS (sized at launch).  Units are
+// enumerated expert by expert in a schedule order; for each position of that
+// order the LDS holds the exclusive prefix of work units.
+//  - Up to kSortMax experts: the experts are taken in order of decreasing row
+//    count (ties by id), so the rounds of a persistent launch start with the
+//    costliest units and end with the cheapest ones, and the last, partly
+//    filled round holds short units; the LDS also caches each expert's
+//    segment start and global scale, so a unit is decoded without a memory
+//    round trip.  Layout: units [E + 1], expert of each position [E],
+//    segment starts [E + 1], global scales [E].
+//  - More experts: id order, units [E + 1] only; segment bounds and global
+//    scales come through the scalar cache.
 extern __shared__ int sched_units[];
-constexpr int kSchedLdsMax = 4 * (kMaxExperts + 1);
-inline int sched_lds_bytes(int64_t num_experts) { return (int)(4 * (num_experts + 1)); }
-
+constexpr int kSortMax = 256;
+constexpr int kSchedLdsMax = 4 * (4 * kSortMax + 2) > 4 * (kMaxExperts + 1)
+                                 ? 4 * (4 * kSortMax + 2)
+                                 : 4 * (kMaxExperts + 1);
+inline int sched_lds_bytes(int64_t num_experts) {
+  return num_experts <= kSortMax ? (int)(4 * (4 * num_experts + 2)) : (int)(4 * (num_experts + 1));
+}
+__device__ __forceinline__ int* sched_perm(int E) { return sched_units + E + 1; }
+__device__ __forceinline__ int* sched_seg(int E) { return sched_units + 2 * E + 1; }
+__device__ __forceinline__ float* sched_g(int E) {
+  return reinterpret_cast<float*>(sched_units + 3 * E + 2);
+}
 struct Sched {
   int tmp[16];
   int flag;
@@ -179,14 +197,15 @@ __device__ __forceinline__ int seg_begin(const GemmParams& p, int e) {
   return p.offsets ? p.offsets[e] : (e == 0 ? 0 : (int)p.rows);
 }
 
-// Fills `sc`; returns the total unit count, or -1 (after flagging the status
-// word) when the offsets are malformed.
+// Fills `sc` and the LDS schedule; returns the total unit count, or -1
+// (after flagging the status word) when the offsets are malformed.
 template <int THREADS, int BM>
 __device__ __forceinline__ int build_schedule(Sched& sc, const GemmParams& p) {
   const int tid = threadIdx.x;
   const int E = p.num_experts;
+  const bool sorted = E <= kSortMax;
   constexpr int PER = (kMaxExperts + THREADS - 1) / THREADS;  // experts per thread
-  int bad = 0, my_units = 0;
+  int bad = 0;
   int cnt[PER];
 #pragma unroll
   for (int t = 0; t < PER; ++t) {
@@ -196,27 +215,66 @@ __device__ __forceinline__ int build_schedule(Sched& sc, const GemmParams& p) {
       const int a = seg_begin(p, e), b = seg_begin(p, e + 1);
       bad |= b < a;
       cnt[t] = (b - a + BM - 1) / BM * p.n_tiles * p.splits;
-      my_units += cnt[t];
+      if (sorted) {
+        sched_seg(E)[e] = a;
+        sched_g(E)[e] = p.g[e];
+      }
     }
   }
-  if (tid == 0) bad |= (seg_begin(p, 0) != 0) || ((int64_t)seg_begin(p, E) != p.rows);
+  if (tid == 0) {
+    bad |= (seg_begin(p, 0) != 0) || ((int64_t)seg_begin(p, E) != p.rows);
+    if (sorted) sched_seg(E)[E] = seg_begin(p, E);
+  }
   bad = __syncthreads_or(bad);
   if (bad) {
     if (blockIdx.x == 0 && tid == 0 && p.d_status != nullptr)
       atomicOr(p.d_status, NVFP4_DSTATUS_BAD_OFFSETS);
     return -1;
   }
+  if (sorted) {
+    // position of expert e: experts with more rows, then equal rows and a
+    // smaller id, come first (the same order in every workgroup); its unit
+    // count goes to that position
+    static_assert(THREADS >= kSortMax, "one expert per thread when sorting");
+    const int* seg = sched_seg(E);
+    if (tid < E) {
+      const int r = seg[tid + 1] - seg[tid];
+      int pos = 0;
+      for (int e2 = 0; e2 < E; ++e2) {
+        const int r2 = seg[e2 + 1] - seg[e2];
+        pos += (r2 > r) || (r2 == r && e2 < tid);
+      }
+      sched_perm(E)[pos] = tid;
+      sched_units[pos] = (r + BM - 1) / BM * p.n_tiles * p.splits;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < PER; ++t) {
+      const int pos = PER * tid + t;
+      cnt[t] = pos < E ? sched_units[pos] : 0;
+    }
+    __syncthreads();
+  }
+  int my_units = 0;
+#pragma unroll
+  for (int t = 0; t < PER; ++t) my_units += cnt[t];
   int total_units;
   int ubase = block_exclusive_scan<THREADS>(my_units, sc.tmp, &total_units);
 #pragma unroll
   for (int t = 0; t < PER; ++t) {
-    const int e = PER * tid + t;
-    if (e < E) sched_units[e] = ubase;
+    const int pos = PER * tid + t;
+    if (pos < E) sched_units[pos] = ubase;
     ubase += cnt[t];
   }
   if (tid == 0) sched_units[E] = total_units;
   __syncthreads();
   return total_units;
+}
+
+// Global scale of expert e.
+__device__ __forceinline__ float expert_g(const GemmParams& p, int e) {
+  return p.num_experts <= kSortMax ? sched_g(p.num_experts)[e]
+                                   : __uint_as_float(sload_u32(p.g, 4u * (uint32_t)e));
 }
 
 struct Unit {
@@ -239,25 +297,35 @@ __device__ __forceinline__ int round_unit(int round, int w, int G) {
 // output tiles (for the split-K counters) are numbered units / splits.
 template <int BM>
 __device__ __forceinline__ Unit decode_unit(const Sched& sc, const GemmParams& p, int unit) {
-  // expert: last e with units[e] <= unit (empty experts have equal bounds)
-  int lo = 0, hi = p.num_experts;
+  // schedule position: last one with units[pos] <= unit (empty experts have
+  // equal bounds)
+  const int E = p.num_experts;
+  int lo = 0, hi = E;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
     if (sched_units[mid] <= unit) lo = mid; else hi = mid;
   }
+  const int pos = __builtin_amdgcn_readfirstlane(lo);
   Unit u;
-  u.e = __builtin_amdgcn_readfirstlane(lo);
-  // segment bounds through the scalar cache: a vector load here would make
-  // the compiler wait for every load in flight, prefetched stages included
-  const int seg0 = p.offsets ? (int)sload_u32(p.offsets, 4u * (uint32_t)u.e) : 0;
-  const int seg1 = p.offsets ? (int)sload_u32(p.offsets, 4u * (uint32_t)(u.e + 1)) : (int)p.rows;
+  int seg0, seg1;
+  if (E <= kSortMax) {
+    u.e = __builtin_amdgcn_readfirstlane(sched_perm(E)[pos]);
+    seg0 = __builtin_amdgcn_readfirstlane(sched_seg(E)[u.e]);
+    seg1 = __builtin_amdgcn_readfirstlane(sched_seg(E)[u.e + 1]);
+  } else {
+    u.e = pos;
+    // segment bounds through the scalar cache: a vector load here would make
+    // the compiler wait for every load in flight, prefetched stages included
+    seg0 = p.offsets ? (int)sload_u32(p.offsets, 4u * (uint32_t)u.e) : 0;
+    seg1 = p.offsets ? (int)sload_u32(p.offsets, 4u * (uint32_t)(u.e + 1)) : (int)p.rows;
+  }
   const int mtiles = (seg1 - seg0 + BM - 1) / BM;
-  const int local = unit - sched_units[u.e];
+  const int local = unit - sched_units[pos];
   const int mt = local % mtiles;
   const int rest = local / mtiles;
   u.ks = rest % p.splits;
   u.nt = rest / p.splits;
-  u.tile = sched_units[u.e] / p.splits + u.nt * mtiles + mt;
+  u.tile = sched_units[pos] / p.splits + u.nt * mtiles + mt;
   u.row0 = seg0 + mt * BM;
   u.row_end = min(u.row0 + BM, seg1);
   u.k_beg = u.ks * p.k_split;
@@ -503,9 +571,10 @@ struct KpLayout {
   // stages of the next unit issued during a unit's last iterations (the
   // other ring slots hold the exchange)
   static constexpr int kPrefetch = NSLOT - kRedSlots;
-  // vector memory instructions of a unit's epilogue (one store per output
-  // element a wave holds after the exchange)
-  static constexpr int kEpiStores = 4 * (BM / 16) * (kNJ / 2);
+  // vector memory instructions of a unit's epilogue when the next unit's
+  // first stages are prefetched: 16-byte stores of the output tile, as many
+  // as the widest output (BM x BN FP32 values) takes per wave
+  static constexpr int kEpiStores = (BM * BN * 4 + 16 * KW * 64 - 1) / (16 * KW * 64);
   static_assert(kWPerWave >= 1 && kSInstr >= 1 && (kSInstr < KW || kSInstr % KW == 0),
                 "load split");
   static_assert(NSLOT <= kWinStages + 1, "window buffers are reused in time");
@@ -765,7 +834,7 @@ __device__ __forceinline__ void kp_kloop(f32x4_t (&acc)[BM / 16][2 * BN / KW / 1
                                          cxg1);
   };
   // loads this wave issued after those of stage lo, through stage hi, plus
-  // the epilogue stores when stage lo was issued before them
+  // the previous unit's epilogue stores when stage lo was issued before them
   auto loads_after = [&](int lo, int hi) {
     int n = (ex && lo < pf) ? E : 0;
 #pragma unroll
@@ -846,6 +915,101 @@ __device__ __forceinline__ void kp_kloop(f32x4_t (&acc)[BM / 16][2 * BN / KW / 1
   }
 }
 
+// Epilogue of a unit without a K split, through LDS.  Wave w holds the
+// summed accumulators of columns [16 NH w, 16 NH (w + 1)) of the unit (NH
+// 16-column tiles, NF 16-row fragments).  Each wave writes its final values
+// (g acc, or SiLU(g acc_gate) (g acc_up) with the 32-row gate/up groups; ESZ
+// bytes each) into a row-major output tile held in the ring slots the
+// exchange used, and the workgroup then writes whole 16-byte pieces of the
+// tile's rows to y, instead of one 2- or 4-byte store per accumulator
+// element.  Every call issues the same number of stores per wave
+// (kEpiStores, what the widest output needs; pieces past the tile, past the
+// unit's rows or past the last column go past the buffer and are dropped),
+// which the next unit's prefetched loads are counted behind.  A slot holds
+// RPS whole rows (a multiple of 4, so the four rows of an accumulator
+// register group share a slot); the pieces of a row sit in slot
+// c ^ ((row >> 2) & MSK), which spreads the accumulator layout's writes (four
+// rows at one column per instruction) over the banks.  The last barrier lets
+// the next unit's loads reuse the slots.
+template <int BM, int NSLOT, int KW, int BN, int ESZ, bool GLU>
+__device__ __forceinline__ void kp_store_tile(const f32x4_t (&out)[BM / 16][BN / KW / 16],
+                                              const GemmParams& p, const Unit& u, float gv,
+                                              uint8_t* ring, int sl0, int wave, int lane) {
+  using L = KpLayout<BM, NSLOT, KW, BN>;
+  constexpr int NF = BM / 16, NH = BN / KW / 16;
+  constexpr int kSt = L::kEpiStores;
+  // opaque copies of the lane and slot indices: otherwise the compiler hoists
+  // this epilogue's address arithmetic above the K loop and keeps it live
+  // there, in registers the loop needs
+  int tid = (int)threadIdx.x;
+  asm volatile("" : "+v"(lane), "+v"(tid), "+s"(sl0), "+s"(wave));
+  constexpr int BNO = GLU ? BN / 2 : BN;  // output columns of the tile
+  constexpr int RB = BNO * ESZ;           // tile row bytes
+  constexpr int CPR = RB / 16;            // 16-byte pieces per row
+  constexpr int MSK = (CPR < 16 ? CPR : 16) - 1;
+  constexpr int RPS = L::kStage / RB;     // tile rows per ring slot
+  static_assert(RPS % 4 == 0 && (BM + RPS - 1) / RPS <= L::kRedSlots, "tile fits the slots");
+  static_assert(CPR >= 4 && (CPR & (CPR - 1)) == 0, "row pieces");
+  const int nout = GLU ? p.n / 2 : p.n;
+  auto row_at = [&](int row) {  // byte address of tile row `row`
+    return ((sl0 + row / RPS) % NSLOT) * L::kStage + (row % RPS) * RB;
+  };
+  const int q = lane >> 4, r16 = lane & 15;
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    const int row4 = f * 16 + 4 * q;
+    const int base = row_at(row4);
+    const int sw = (row4 >> 2) & MSK;
+#pragma unroll
+    for (int jj = 0; jj < NH; ++jj) {
+      if (GLU && (jj & 1)) continue;
+      const int col = wave * (NH * 16) + jj * 16 + r16;  // weight row within the unit
+      const int ob = (GLU ? (col - r16) / 2 + r16 : col) * ESZ;
+      uint8_t* dst = ring + base + ((((ob >> 4) ^ sw)) << 4) + (ob & 15);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v;
+        if constexpr (!GLU) {
+          v = gv * out[f][jj][r];
+        } else {
+          const float gate = gv * out[f][jj][r];
+          const float up = gv * out[f][(jj + 1) % NH][r];
+          // SiLU(gate) = gate / (1 + e^-gate) on the hardware exp2 and
+          // reciprocal (relative error ~1e-6, inside the FP32 bound)
+          const float e = __builtin_amdgcn_exp2f(-gate * 1.4426950408889634f);
+          v = gate * __builtin_amdgcn_rcpf(1.0f + e) * up;
+        }
+        if constexpr (ESZ == 4) *reinterpret_cast<float*>(dst + r * RB) = v;
+        else *reinterpret_cast<uint16_t*>(dst + r * RB) = (uint16_t)float_to_bf16_rne(v);
+      }
+    }
+  }
+  __syncthreads();
+  const int rows = u.row_end - u.row0;
+  const int col_bytes = u.nt * RB;  // first byte of the tile within a row of y
+  const int row_bytes = nout * ESZ;
+  u32x4_t v[kSt];
+  uint32_t off[kSt];
+#pragma unroll
+  for (int i = 0; i < kSt; ++i) {
+    const int ci = tid + i * (KW * 64);
+    const int row = ci / CPR, c = ci % CPR;
+    v[i] = u32x4_t{0u, 0u, 0u, 0u};
+    off[i] = kOffNone;
+    if (row < BM) {
+      v[i] = *reinterpret_cast<const u32x4_t*>(ring + row_at(row) + ((c ^ ((row >> 2) & MSK)) << 4));
+      if (row < rows && col_bytes + 16 * c < row_bytes)
+        off[i] = (uint32_t)(row * row_bytes + col_bytes + 16 * c);
+    }
+  }
+  __syncthreads();
+  const __amdgpu_buffer_rsrc_t ry =
+      make_rsrc(static_cast<const char*>(p.y) + (int64_t)u.row0 * row_bytes,
+                (uint32_t)(rows * row_bytes));
+#pragma unroll
+  for (int i = 0; i < kSt; ++i) __builtin_amdgcn_raw_buffer_store_b128(v[i], ry, off[i], 0, 0);
+}
+
 // GATHER: activation rows come through p.row_index (see kp_gather).
 template <int BM, int NSLOT, int KW, int BN, bool GATHER = false>
 __global__ __launch_bounds__(KW * 64) void gemm_kp_kernel(GemmParams p) {
@@ -867,9 +1031,12 @@ __global__ __launch_bounds__(KW * 64) void gemm_kp_kernel(GemmParams p) {
   const int first = round_unit(0, blockIdx.x, G);
   if (total <= 0 || first >= total) return;
   const KpOffsets<BM, KW, BN> off = kp_offsets<BM, NSLOT, KW, BN>(p.k, wave, lane);
-  // the next unit's first stages are prefetched only when the epilogue's
-  // store count is fixed (no K split, output addressable by buffer stores)
-  const bool can_pf = p.splits == 1 && p.n <= kFixedStoreMaxN;
+  // the epilogue goes through LDS (a fixed number of 16-byte stores) when
+  // there is no K split, the output is addressable by buffer stores and its
+  // rows split into whole 16-byte pieces; only then are the next unit's
+  // first stages prefetched, behind that fixed store count
+  const int nout_bytes = (p.act ? p.n / 2 : p.n) * (p.out_f32 ? 4 : 2);
+  const bool can_pf = p.splits == 1 && p.n <= kFixedStoreMaxN && nout_bytes % 16 == 0;
 
   int round = 0;
   Unit u = decode_unit<BM>(sc, p, first);
@@ -889,7 +1056,7 @@ __global__ __launch_bounds__(KW * 64) void gemm_kp_kernel(GemmParams p) {
       if constexpr (GATHER) kp_gather<BM, NSLOT, KW, BN>(nx, nxg, p, un, wave, lane);
     }
     const int pn = (has_next && can_pf && cu.nch >= NSLOT) ? min(L::kPrefetch, nx.nch) : 0;
-    const float gv = __uint_as_float(sload_u32(p.g, 4u * (uint32_t)u.e));
+    const float gv = expert_g(p, u.e);
     // 16-row fragments holding rows of this tile (the rest is padding)
     const int nf = min(NF, (u.row_end - u.row0 + 15) / 16);
 
@@ -946,7 +1113,17 @@ __global__ __launch_bounds__(KW * 64) void gemm_kp_kernel(GemmParams p) {
     }
     __syncthreads();  // exchange chunks read before the next unit's loads reuse them
     // wave w now owns columns [w CPW/2, (w + 1) CPW/2) of the unit
-    finish_tile<NF, NH, KW, BN>(out, p, u, gv, sc);
+    if (can_pf) {
+      const int sl0 = (sb0 + cu.nch + pn) % NSLOT;
+      if (p.act) {
+        if (p.out_f32) kp_store_tile<BM, NSLOT, KW, BN, 4, true>(out, p, u, gv, ring, sl0, wave, lane);
+        else kp_store_tile<BM, NSLOT, KW, BN, 2, true>(out, p, u, gv, ring, sl0, wave, lane);
+      } else {
+        if (p.out_f32) kp_store_tile<BM, NSLOT, KW, BN, 4, false>(out, p, u, gv, ring, sl0, wave, lane);
+        else kp_store_tile<BM, NSLOT, KW, BN, 2, false>(out, p, u, gv, ring, sl0, wave, lane);
+      }
+    } else
+      finish_tile<NF, NH, KW, BN>(out, p, u, gv, sc);
     if (!has_next) break;
     sb0 = (sb0 + cu.nch) % NSLOT;
     wb0 = (wb0 + (cu.nch + L::kWinStages - 1) / L::kWinStages) % L::kWinBufs;
@@ -1395,7 +1572,7 @@ __global__ __launch_bounds__(kRegThreads) void gemm_reg_kernel(GemmParams p) {
       if (more2) store_xtile<BM>(xs[0], xr, tid);
       __syncthreads();
     }
-    finish_tile<NF, kNW, kRegWaves, kRegBN>(acc, p, u, p.g[u.e], sc);
+    finish_tile<NF, kNW, kRegWaves, kRegBN>(acc, p, u, expert_g(p, u.e), sc);
   }
 }
 

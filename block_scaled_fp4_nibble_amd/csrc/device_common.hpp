@@ -44,6 +44,36 @@ __device__ __forceinline__ uint32_t encode_e4m3(float x) {
   return code > 0x7Eu ? 0x7Eu : code;
 }
 
+// Correctly rounded FP32 quotient |x| / d for the element encoder (d > 0).
+// Where d lies in [2^-98, 2^100] (`fast`), it is formed from the correctly
+// rounded reciprocal r = RN(1/d) with one FMA-based correction (Markstein's
+// method: q0 = RN(|x| r), e = |x| - q0 d exactly, q = RN(q0 + e r), which is
+// RN(|x| / d) for normal operands); otherwise, and for d == 0 (quotient 0),
+// the IEEE division is used.
+__device__ __forceinline__ bool element_divisor(float d, float& r) {
+  const bool fast = d >= 0x1p-98f && d <= 0x1p100f;
+  r = fast ? 1.0f / d : 0.0f;  // IEEE division: correctly rounded
+  return fast;
+}
+__device__ __forceinline__ float element_quotient(float x, float d, float r, bool fast) {
+  const float ax = __builtin_fabsf(x);
+  if (fast) {
+    const float q0 = ax * r;
+    return __builtin_fmaf(__builtin_fmaf(-q0, d, ax), r, q0);
+  }
+  return d != 0.0f ? ax / d : 0.0f;
+}
+
+// Two E2M1 codes into nibbles 2 SEL and 2 SEL + 1 of `word`: gfx950's FP32 ->
+// FP4 pack conversion with scale operand 1.0 gives the sign bit of each input
+// followed by its nearest E2M1 magnitude, ties to the even code (0.25 -> 0,
+// 0.75 -> 1, 1.25 -> 1, 1.75 -> 2, 2.5 -> 2, 3.5 -> 4, 5 -> 4), saturating at
+// 6; the sign is kept on a zero magnitude.
+template <int SEL>
+__device__ __forceinline__ uint32_t pack_e2m1_pair(uint32_t word, float q0, float q1) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, q0, q1, 1.0f, SEL);
+}
+
 // ---- decoders ---------------------------------------------------------------
 
 // E4M3 byte `sel` (0..3) of a dword to float (gfx950 converts OCP E4M3FN).

@@ -1767,6 +1767,10 @@ GemmPlan plan_gemm(int64_t rows, int64_t num_experts, int64_t n, int64_t k, bool
   pl.max_tiles = (int)max_tiles;
   const int64_t units_bound = max_tiles * splits;
   pl.grid = (int)std::max<int64_t>(1, std::min<int64_t>(slots, units_bound));
+  // tuning / test override: cap the persistent grid, so that every workgroup
+  // walks several units (rounds, cross-unit prefetch) even on small products
+  const int force_grid = env_int("NVFP4_GRID", 0);
+  if (force_grid > 0) pl.grid = std::min(pl.grid, force_grid);
   pl.ws_bytes = splits > 1
                     ? kCounterBytes + (size_t)max_tiles * splits * bm * pl.bn * sizeof(float)
                     : 0;

@@ -110,18 +110,14 @@ __device__ __forceinline__ void encode_block(u32x4_t v0, u32x4_t v1, float g, ui
   }
   const float s_dec = decode_e4m3<0>(scode);
   const float d = s_dec * g;
-  const bool fast = d >= 0x1p-98f && d <= 0x1p100f;
-  const float r = fast ? 1.0f / d : 0.0f;
+  float r;
+  const bool fast = element_divisor(d, r);
 
-  // Each pair of elements: the FP32 quotients |w| / d (Markstein or IEEE
-  // division, as above; 0 when d == 0) take the sign of w, and gfx950's
-  // FP32 -> E2M1 pack conversion (scale operand 1.0) turns them into codes:
-  // the sign bit, then the nearest E2M1 magnitude with ties to the even code
-  // (0.25 -> 0, 0.75 -> 1, 1.25 -> 1, 1.75 -> 2, 2.5 -> 2, 3.5 -> 4, 5 -> 4),
-  // saturating at 6, with the sign kept on a zero magnitude.  A GPU probe
-  // compared it with a bit-manipulation encoder of that rule on every finite
-  // non-negative FP32 pattern, +inf and their negatives: no difference.
-  // Element 2j goes to the low nibble of byte j.
+  // Each pair of elements: the FP32 quotients |w| / d (element_quotient),
+  // signed like w, become two E2M1 codes (pack_e2m1_pair); element 2j goes
+  // to the low nibble of byte j.  The pack conversion and the quotient are
+  // compared with the oracle's definition over every FP32 input pattern and
+  // with IEEE division by the GPU tests (tests/test_gpu_conversions.py).
   uint32_t words[2] = {0u, 0u};
 #pragma unroll
   for (int e = 0; e < 16; e += 2) {
@@ -129,22 +125,13 @@ __device__ __forceinline__ void encode_block(u32x4_t v0, u32x4_t v1, float g, ui
     const float xs[2] = {__uint_as_float(dw << 16), __uint_as_float(dw & 0xFFFF0000u)};
     float q[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const float x = __builtin_fabsf(xs[i]);
-      float qi = 0.0f;
-      if (fast) {
-        const float q0 = x * r;
-        qi = __builtin_fmaf(__builtin_fmaf(-q0, d, x), r, q0);
-      } else if (d != 0.0f) {
-        qi = x / d;
-      }
-      q[i] = __builtin_copysignf(qi, xs[i]);
-    }
+    for (int i = 0; i < 2; ++i)
+      q[i] = __builtin_copysignf(element_quotient(xs[i], d, r, fast), xs[i]);
     switch ((e % 8) / 2) {
-      case 0: words[e / 8] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(words[e / 8], q[0], q[1], 1.0f, 0); break;
-      case 1: words[e / 8] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(words[e / 8], q[0], q[1], 1.0f, 1); break;
-      case 2: words[e / 8] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(words[e / 8], q[0], q[1], 1.0f, 2); break;
-      default: words[e / 8] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(words[e / 8], q[0], q[1], 1.0f, 3); break;
+      case 0: words[e / 8] = pack_e2m1_pair<0>(words[e / 8], q[0], q[1]); break;
+      case 1: words[e / 8] = pack_e2m1_pair<1>(words[e / 8], q[0], q[1]); break;
+      case 2: words[e / 8] = pack_e2m1_pair<2>(words[e / 8], q[0], q[1]); break;
+      default: words[e / 8] = pack_e2m1_pair<3>(words[e / 8], q[0], q[1]); break;
     }
   }
   u32x2_t outw = {words[0], words[1]};

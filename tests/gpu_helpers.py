@@ -75,3 +75,63 @@ def sample_positions(rows: int, cols: int, count: int, seed: int):
     r = np.concatenate([r, [0, rows - 1, 0, rows - 1]])
     c = np.concatenate([c, [0, 0, cols - 1, cols - 1]])
     return r.astype(np.int64), c.astype(np.int64)
+
+
+def stratified_positions(segments, cols, seed, blk_r=16, blk_c=64):
+    """Sample output positions that hit every 16-row x 64-column block of every
+    row segment (an expert's rows, or [(0, rows)] for a dense product) once,
+    so every output tile, every persistent round and every wave's column range
+    of any kernel configuration gets a sample.  The position inside the block
+    cycles through the (row % 16, column % 64) classes of the accumulator
+    layout, so all of them are covered across the blocks; each segment's last
+    row and the last column are always included."""
+    rng = np.random.default_rng(np.random.SeedSequence([4321, seed]))
+    rows_out, cols_out = [], []
+    k = int(rng.integers(0, 1 << 20))
+    for a, b in segments:
+        a, b = int(a), int(b)
+        if b <= a:
+            continue
+        for r0 in range(a, b, blk_r):
+            nr = min(blk_r, b - r0)
+            for c0 in range(0, cols, blk_c):
+                nc = min(blk_c, cols - c0)
+                rows_out.append(r0 + (k % blk_r) % nr)
+                cols_out.append(c0 + ((k // blk_r) % blk_c) % nc)
+                k += 1
+        rows_out += [b - 1, b - 1, a]
+        cols_out += [cols - 1, 0, cols - 1]
+    return np.asarray(rows_out, np.int64), np.asarray(cols_out, np.int64)
+
+
+def segments_of(offsets):
+    off = np.asarray(offsets)
+    return [(int(off[e]), int(off[e + 1])) for e in range(len(off) - 1)]
+
+
+class EnvOverride:
+    """Set library tuning overrides (environment variables read per call) for
+    a block and restore them afterwards."""
+
+    def __init__(self, **kv):
+        self.kv = {k: (None if v is None else str(v)) for k, v in kv.items()}
+        self.old = {}
+
+    def __enter__(self):
+        import os
+        for k, v in self.kv.items():
+            self.old[k] = os.environ.get(k)
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+        return self
+
+    def __exit__(self, *exc):
+        import os
+        for k, v in self.old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+        return False

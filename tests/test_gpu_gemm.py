@@ -192,16 +192,27 @@ def test_zero_weight_gives_exact_zero():
     assert (host(y) == 0).all()
 
 
-def test_large_sampled():
-    """8192 x 8192 x 8192: 4100 sampled outputs against the oracle."""
+def test_large_stratified_and_full_tiles():
+    """8192 x 8192 x 8192 on the 256 x 256 large-M kernel (four persistent
+    rounds of 256 tiles): one output in every 16 x 64 block (all tiles,
+    rounds and accumulator positions), every output written, and four whole
+    256 x 256 tiles -- one from each round -- against the oracle."""
     nv = require_gpu()
+    from gpu_helpers import BF16_TOL, normalized_error, stratified_positions
     x, w = W.large_dense()
     p, s, g = oracle_weight(w)
     y = run_gemm(nv, x, to_qw(nv, p, s, g), torch.bfloat16)
-    rows, cols = sample_positions(8192, 8192, 4096, seed=5)
-    y_ref, d = oracle.gemm_sampled(x, p, s, g[0], rows, cols)
     yv = output_values(y)
     assert np.isfinite(yv).all()  # every element written
-    from gpu_helpers import normalized_error, BF16_TOL
+    rows, cols = stratified_positions([(0, 8192)], 8192, seed=5)
+    y_ref, d = oracle.gemm_sampled(x, p, s, g[0], rows, cols)
     err = normalized_error(yv[rows, cols], y_ref, d)
     assert err <= BF16_TOL, err
+    # tile t covers rows 256 (t // 32), columns 256 (t % 32); round r of a
+    # 256-workgroup grid takes tiles [256 r, 256 r + 256)
+    for rnd in range(4):
+        t = 256 * rnd + (37 * rnd + 11) % 256
+        r0, c0 = 256 * (t // 32), 256 * (t % 32)
+        y_ref, d = oracle.gemm(x[r0:r0 + 256], p[c0:c0 + 256], s[c0:c0 + 256], g[0])
+        err = normalized_error(yv[r0:r0 + 256, c0:c0 + 256], y_ref, d)
+        assert err <= BF16_TOL, "tile %d: %.3e" % (t, err)

@@ -15,7 +15,8 @@ import torch
 import oracle
 import workloads as W
 from gpu_helpers import (BF16_TOL, F32_TOL, check_close, dev, host, normalized_error,
-                         output_values, require_gpu, sample_positions)
+                         output_values, require_gpu, segments_of,
+                         stratified_positions)
 
 pytestmark = pytest.mark.gpu
 
@@ -90,11 +91,14 @@ def test_forced_split_k(counts, n, k, splits):
     assert np.array_equal(host(y1).view(np.uint32), host(y2).view(np.uint32)), "not reproducible"
 
 
-def _sampled_check(nv, x, r, p, s, g, out_dtype, seed, count=3000):
+def _sampled_check(nv, x, r, p, s, g, out_dtype, seed):
     y = run_grouped(nv, x, r.offsets, to_qw(nv, p, s, g), out_dtype)
     yv = output_values(y)
     assert np.isfinite(yv).all(), "a routed row was not written"
-    rows, cols = sample_positions(r.rows, yv.shape[1], count, seed)
+    # one output in every 16 x 64 block of every expert's rows (so every unit,
+    # persistent round and wave column range), cycling through the
+    # accumulator layout's positions
+    rows, cols = stratified_positions(segments_of(r.offsets), yv.shape[1], seed)
     y_ref, d = oracle.grouped_gemm_sampled(x, r.offsets, p, s, g, rows, cols)
     err = normalized_error(yv[rows, cols], y_ref, d)
     tol = F32_TOL if out_dtype == torch.float32 else BF16_TOL
@@ -166,6 +170,20 @@ def test_zipf_hot_expert_full(moe_zipf_up):
     r0, r1 = r.offsets[e], r.offsets[e + 1]
     y_ref, d = oracle.gemm(x[r0:r1], p[e], s[e], g[e])
     assert normalized_error(y[r0:r1], y_ref, d) <= F32_TOL
+
+
+def test_zipf_down_full_experts(moe_zipf_down):
+    """Every output of the down launch's hottest expert (several row tiles),
+    of its median expert and of its smallest one."""
+    nv = require_gpu()
+    r, h, p, s, g = moe_zipf_down
+    y = output_values(run_grouped(nv, h, r.offsets, to_qw(nv, p, s, g), torch.float32))
+    order = np.argsort(r.counts, kind="stable")
+    for e in (int(order[-1]), int(order[len(order) // 2]), int(order[0])):
+        r0, r1 = r.offsets[e], r.offsets[e + 1]
+        y_ref, d = oracle.gemm(h[r0:r1], p[e], s[e], g[e])
+        err = normalized_error(y[r0:r1], y_ref, d)
+        assert err <= F32_TOL, "expert %d (%d rows): %.3e" % (e, r1 - r0, err)
 
 
 def test_zipf_with_empty_experts():

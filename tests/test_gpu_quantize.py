@@ -53,6 +53,18 @@ def test_batched_experts_full_size():
     assert_same(w, "64x4096x6144 experts")
 
 
+def test_zipf_up_weights_full_size():
+    """64 experts of 4096 x 6144 (the ~64 tok/expert up-projection weights)."""
+    _, _, w = W.moe_zipf_up_inputs()
+    assert_same(w, "zipf up 64x4096x6144")
+
+
+def test_zipf_down_weights_full_size():
+    """64 experts of 6144 x 2048 (the ~64 tok/expert down-projection weights)."""
+    _, _, w = W.moe_zipf_down_inputs()
+    assert_same(w, "zipf down 64x6144x2048")
+
+
 def test_large_weight():
     _, w = W.large_dense()
     assert_same(w, "8192x8192")

@@ -34,7 +34,7 @@ MAX_EXPERTS = 1024
 EXPORTED = [
     "nvfp4_quantize", "nvfp4_gemm", "nvfp4_grouped_gemm", "nvfp4_grouped_gemm_swiglu",
     "nvfp4_grouped_gemm_gather", "nvfp4_moe_combine", "nvfp4_gemm_w4a4",
-    "nvfp4_grouped_gemm_w4a4", "nvfp4_gemm_w4a4_workspace_size",
+    "nvfp4_grouped_gemm_w4a4", "nvfp4_gemm_noalloc", "nvfp4_gemm_w4a4_workspace_size",
     "nvfp4_grouped_gemm_w4a4_workspace_size",
     "nvfp4_quantize_workspace_size",
     "nvfp4_gemm_workspace_size", "nvfp4_grouped_gemm_workspace_size",
@@ -83,6 +83,8 @@ def load_library(path: str = LIB_PATH):
         lib.nvfp4_grouped_gemm_w4a4.argtypes = [P, P, P, I64, P, I64, I64, I64, P, P, P, P, I32,
                                                 P, P, SZ, P]
         lib.nvfp4_grouped_gemm_w4a4.restype = I32
+        lib.nvfp4_gemm_noalloc.argtypes = [P, I64, I64, I64, P, P, P, P, I32, P]
+        lib.nvfp4_gemm_noalloc.restype = I32
         lib.nvfp4_gemm_w4a4_workspace_size.argtypes = [I64, I64, I64]
         lib.nvfp4_gemm_w4a4_workspace_size.restype = SZ
         lib.nvfp4_grouped_gemm_w4a4_workspace_size.argtypes = [I64, I64, I64, I64]
@@ -142,6 +144,11 @@ def nvfp4_gemm(x, m, n, k, packed, scales, global_scale, y, out, workspace, ws_b
     return load_library().nvfp4_gemm(_ptr(x), m, n, k, _ptr(packed), _ptr(scales),
                                      _ptr(global_scale), _ptr(y), out, _ptr(workspace), ws_bytes,
                                      _stream(stream))
+
+
+def nvfp4_gemm_noalloc(x, m, n, k, packed, scales, global_scale, y, out, stream=None):
+    return load_library().nvfp4_gemm_noalloc(_ptr(x), m, n, k, _ptr(packed), _ptr(scales),
+                                             _ptr(global_scale), _ptr(y), out, _stream(stream))
 
 
 def nvfp4_grouped_gemm(x, rows, offsets, num_experts, n, k, packed, scales, global_scales, y,

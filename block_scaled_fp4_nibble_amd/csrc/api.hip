@@ -225,6 +225,58 @@ nvfp4_status_t nvfp4_grouped_gemm_swiglu(const void* x_bf16, int64_t rows,
                   reinterpret_cast<hipStream_t>(stream), true, 1);
 }
 
+// ---- GEMM without allocation ------------------------------------------------
+
+namespace {
+// Scratch of nvfp4_gemm_noalloc: the split-K tile counters (the first
+// kCounterBytes, zero at rest) and the partial tiles, in one array per device
+// that the library's code object holds from load to process end.
+constexpr size_t kScratchBytes = NVFP4_NOALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes > nvfp4::kCounterBytes, "counters fit the scratch");
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+// Per device: the scratch array's device address (in host code the array's
+// name is only a stand-in for the symbol) once looked up and its counter
+// region zeroed.
+void* g_scratch_ptr[kMaxDevices] = {nullptr};
+
+nvfp4_status_t scratch_ptr(hipStream_t stream, void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return NVFP4_ERR_HIP;
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return NVFP4_ERR_HIP;
+    // counters must start at zero (a fill kernel, not a memset node, so this
+    // may run under stream capture); completed calls leave them zero
+    if (nvfp4::launch_fill_zero(ptr, nvfp4::kCounterBytes, stream) != hipSuccess)
+      return NVFP4_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return NVFP4_OK;
+}
+}  // namespace
+
+nvfp4_status_t nvfp4_gemm_noalloc(const void* x_bf16, int64_t m, int64_t n, int64_t k,
+                                  const uint8_t* packed, const uint8_t* scales,
+                                  const float* global_scale, void* y, nvfp4_out_t out,
+                                  void* stream) {
+  nvfp4_status_t st = check_gemm_common(x_bf16, m, n, k, packed, scales, global_scale, y, out);
+  if (st != NVFP4_OK || m == 0) return st;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const size_t need = nvfp4::plan_gemm(m, 1, n, k, false, cu_count()).ws_bytes;
+  if (need > kScratchBytes) return NVFP4_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  if (need > 0) {
+    st = scratch_ptr(s, &ws);
+    if (st != NVFP4_OK) return st;
+  }
+  return run_gemm(x_bf16, m, nullptr, 1, n, k, packed, scales, global_scale, y, out, nullptr, ws,
+                  need > 0 ? kScratchBytes : 0, s, false);
+}
+
 // ---- W4A4 -----------------------------------------------------------------
 
 namespace {

@@ -47,8 +47,9 @@
  * Conventions
  * -----------
  *  - Ownership: the caller owns every buffer.  The library allocates no
- *    device or host memory; the only state it keeps is cached device
- *    properties (compute-unit count) per device.
+ *    device or host memory; the state it keeps is cached device properties
+ *    (compute-unit count) per device and, for nvfp4_gemm_noalloc only, one
+ *    fixed scratch array per device that its code object holds.
  *  - Pointers are device pointers unless stated otherwise; `stream` is a
  *    hipStream_t (NULL means the default stream).  Every call only enqueues
  *    work on `stream` and returns without waiting for it.
@@ -234,6 +235,25 @@ nvfp4_status_t nvfp4_grouped_gemm_w4a4(const uint8_t* x_packed, const uint8_t* x
 size_t nvfp4_gemm_w4a4_workspace_size(int64_t m, int64_t n, int64_t k);
 size_t nvfp4_grouped_gemm_w4a4_workspace_size(int64_t rows, int64_t num_experts, int64_t n,
                                               int64_t k);
+
+/* Dense W4A16 GEMM for callers that cannot allocate device memory or pass a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments, result and error behaviour as
+ * nvfp4_gemm (bit-identical output: the same schedule and kernels), without
+ * the workspace: the split-K counters and partial tiles live in a scratch
+ * array inside the library, one per GPU, of NVFP4_NOALLOC_SCRATCH_BYTES bytes
+ * (64 KiB of counters + 16 MiB of partial tiles), held from the library's
+ * load until the process ends.  A shape whose schedule needs more returns
+ * NVFP4_ERR_UNSUPPORTED and enqueues nothing.  The call allocates nothing;
+ * its first call on a device looks up that device's array and zeroes the
+ * counter region with a fill kernel on `stream` (no memset node).  All calls
+ * on one GPU share its array: calls that may overlap on one GPU (several
+ * streams, or host threads) race and must be serialized by the caller. */
+#define NVFP4_NOALLOC_SCRATCH_BYTES ((size_t)65536 + ((size_t)16 << 20))
+nvfp4_status_t nvfp4_gemm_noalloc(const void* x_bf16, int64_t m, int64_t n, int64_t k,
+                                  const uint8_t* packed, const uint8_t* scales,
+                                  const float* global_scale, void* y, nvfp4_out_t out,
+                                  void* stream);
 
 /* Workspace sizes (bytes) for the calls above; 0 means none is needed.  The
  * sizes depend on the current device's compute-unit count. */

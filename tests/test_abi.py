@@ -93,6 +93,17 @@ def test_gemm_host_validation(lib):
     assert gemm_call(m=0, x=None, y=None) == 0  # empty problem is a no-op
 
 
+def test_gemm_noalloc_host_validation(lib):
+    def call(x=A, m=4, n=8, k=32, y=A, out=nv.OUT_BF16):
+        return nv.nvfp4_gemm_noalloc(x, m, n, k, A, A, A, y, out, S)
+    assert call(k=24) == 1
+    assert call(n=0) == 1
+    assert call(out=7) == 1
+    assert call(x=None) == 1
+    assert call(y=MIS) == 2
+    assert call(m=0, x=None, y=None) == 0
+
+
 def test_grouped_host_validation(lib):
     def call(E=4, offsets=A, rows=8, k=32):
         return nv.nvfp4_grouped_gemm(A, rows, offsets, E, 8, k, A, A, A, A, nv.OUT_BF16, None,

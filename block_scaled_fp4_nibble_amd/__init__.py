@@ -255,22 +255,45 @@ class QuantizedWeight:
 
 
 class Workspace:
-    """Grow-only device workspace whose counter region is zeroed once at
-    allocation (the kernels leave it zeroed after every call)."""
+    """Device workspaces for the convenience layer, one per (device, stream):
+    calls on different streams never share split-K counters (the C contract:
+    calls that may run concurrently need separate workspaces).
+
+    Eager calls grow a stream's buffer as shapes grow and zero its counter
+    region once at allocation (the kernels leave it zeroed after every call).
+    An outgrown buffer is kept alive, because a HIP graph captured earlier may
+    still hold its address.  Calls made while the stream is being captured get
+    a fresh buffer of their own whose counter zeroing is recorded in the graph
+    (a fill kernel, so it runs at every replay); such buffers are never handed
+    to eager calls, whose counters could otherwise be read before the first
+    replay zeroed them, and are kept alive as long as the process."""
 
     def __init__(self):
         self._buf = {}
+        self._keep = []
+        self._lock = threading.Lock()
 
     def get(self, nbytes: int, device, stream=None):
         if nbytes == 0:
             return None
-        key = torch.device(device).index
-        buf = self._buf.get(key)
-        if buf is None or buf.numel() < nbytes:
-            buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        dev = torch.device(device).index
+        handle = _stream(stream).value or 0
+        if torch.cuda.is_current_stream_capturing():
+            buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
             _check(nvfp4_workspace_init(buf, buf.numel(), stream), "nvfp4_workspace_init")
-            self._buf[key] = buf
-        return buf
+            with self._lock:
+                self._keep.append(buf)
+            return buf
+        key = (dev, handle)
+        with self._lock:
+            buf = self._buf.get(key)
+            if buf is None or buf.numel() < nbytes:
+                new = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+                _check(nvfp4_workspace_init(new, new.numel(), stream), "nvfp4_workspace_init")
+                if buf is not None:
+                    self._keep.append(buf)
+                self._buf[key] = buf = new
+            return buf
 
 
 _gemm_ws = Workspace()

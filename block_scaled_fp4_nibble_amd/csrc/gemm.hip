@@ -52,6 +52,7 @@
 #include <cstdlib>
 
 #include "device_common.hpp"
+#include "kp_layout.hpp"
 #include "nvfp4_internal.hpp"
 
 namespace nvfp4 {
@@ -485,7 +486,6 @@ __device__ __forceinline__ bool finish_tile(f32x4_t (&acc)[NF][NW], const GemmPa
 
 // ---- staged-ring pieces (k % 64 == 0) ---------------------------------------------
 
-constexpr int kRingKC = 128;       // K per stage
 
 // s_waitcnt vmcnt(n) for a run-time n: the immediate must be a constant.
 // Encoding (gfx9): vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt
@@ -540,50 +540,12 @@ __device__ __forceinline__ void wait_vmcnt_c() {
 // LDS swizzles (chosen for gfx950's ds_read_b128 / ds_read_b64 bank mapping):
 // activation row r keeps its 16-byte chunk c in slot c ^ (r & 15); weight row
 // R keeps its 16-byte chunk c in slot c ^ ((R >> 2) & 3).
+// LDS budget of every K-phase configuration: ring, scale windows, the
+// workgroup's schedule scratch and the largest dynamic schedule.
 template <int BM, int NSLOT, int KW, int BN>
-struct KpLayout {
-  static constexpr int kCPW = 2 * BN / KW;          // columns per wave
-  static constexpr int kNJ = kCPW / 16;             // MFMA column tiles per wave
-  static constexpr int kW = 0;                      // BN rows x 64 B packed nibbles
-  static constexpr int kX = BN * 64;                // BM rows x 256 B activations
-  static constexpr int kStage = kX + BM * 256;
-  static constexpr int kWPerWave = BN / 16 / KW;    // 1 KB (16-row) weight loads per wave
-  static constexpr int kXInstr = BM / 4;            // 1 KB (4-row) activation loads
-  static constexpr int kXPerWave = kXInstr >= KW ? kXInstr / KW : 1;
-  static constexpr int kLoadsPerStage = kWPerWave + kXPerWave;
-  // A scale window covers kWinStages stages (8 bytes per row each) of one
-  // unit and goes out just before its first stage.  Windows take three
-  // buffers in stream order; a buffer is refilled three windows later, after
-  // every wave has read the window it held (NSLOT <= kWinStages + 1 keeps
-  // that true even across units whose last window is short).
-  static constexpr int kWinStages = NSLOT <= 3 ? 2 : 4;
-  static constexpr int kWinBufs = 3;
-  static constexpr int kWinRow = 8 * kWinStages;    // window bytes per weight row
-  static constexpr int kWinBytes = BN * kWinRow;
-  static constexpr int kSInstr = kWinBytes / 1024;  // 1 KB scale window loads
-  static constexpr int kSWin = NSLOT * kStage;
-  static constexpr int kTotal = kSWin + kWinBufs * kWinBytes;
-  static constexpr int kSPerWave = kSInstr >= KW ? kSInstr / KW : 1;
-  // K-half exchange at the end of a unit: 1 KB chunks, kRedSlots ring slots
-  static constexpr int kChunksPerStage = kStage / 1024;
-  static constexpr int kRedChunks = KW * (BM / 16) * (kNJ / 2);
-  static constexpr int kRedSlots = (kRedChunks + kChunksPerStage - 1) / kChunksPerStage;
-  // stages of the next unit issued during a unit's last iterations (the
-  // other ring slots hold the exchange)
-  static constexpr int kPrefetch = NSLOT - kRedSlots;
-  // vector memory instructions of a unit's epilogue when the next unit's
-  // first stages are prefetched: 16-byte stores of the output tile, as many
-  // as the widest output (BM x BN FP32 values) takes per wave
-  static constexpr int kEpiStores = (BM * BN * 4 + 16 * KW * 64 - 1) / (16 * KW * 64);
-  static_assert(kWPerWave >= 1 && kSInstr >= 1 && (kSInstr < KW || kSInstr % KW == 0),
-                "load split");
-  static_assert(NSLOT <= kWinStages + 1, "window buffers are reused in time");
-  static_assert(kNJ % 2 == 0, "column tiles split between the K halves");
-  static_assert(NSLOT >= 3 && NSLOT <= 5, "windows are issued one window ahead");
-  static_assert(kTotal + (int)sizeof(Sched) + kSchedLdsMax <= 160 * 1024, "LDS budget");
-  static_assert(kStage % 1024 == 0 && kRedSlots < NSLOT, "exchange fits the ring");
-  static_assert(kPrefetch >= 1 && kPrefetch <= kWinStages, "prefetch within window 0");
-};
+constexpr bool kp_fits_lds() {
+  return KpLayout<BM, NSLOT, KW, BN>::kTotal + (int)sizeof(Sched) + kSchedLdsMax <= 160 * 1024;
+}
 
 template <int BM, int KW, int BN>
 struct KpOffsets {
@@ -1014,6 +976,7 @@ __device__ __forceinline__ void kp_store_tile(const f32x4_t (&out)[BM / 16][BN /
 template <int BM, int NSLOT, int KW, int BN, bool GATHER = false>
 __global__ __launch_bounds__(KW * 64) void gemm_kp_kernel(GemmParams p) {
   using L = KpLayout<BM, NSLOT, KW, BN>;
+  static_assert(kp_fits_lds<BM, NSLOT, KW, BN>(), "LDS budget");
   constexpr int NF = BM / 16;
   constexpr int NJ = L::kNJ;
   constexpr int NH = NJ / 2;  // column tiles a wave keeps after the K-half exchange

@@ -19,7 +19,8 @@ Output: one JSON line.  value = useful TFLOPS of the step (2 * rows * N * K
 summed over the three launches, divided by wall time of the timed steps);
 roofline = algorithmic HBM bytes per launch of the dominant kernel over its
 average launch time (HIP events on the launch stream), against 8 TB/s;
-cpu_baseline = the CPU oracle timed on a bounded sample of launch 1.
+cpu_baseline = the CPU oracle timed on a bounded sample of launch 1 (plus its
+quantize, and single-thread figures for the small dense and decode shapes).
 """
 from __future__ import annotations
 
@@ -110,32 +111,10 @@ def build_workload():
         launches.append(dict(name=name, qw=qw, x=x, off=off, y=y, n=n, k=k, rows=r.rows,
                              counts=r.counts.tolist(), experts=E, tokens=r.tokens,
                              row_token=torch.from_numpy(r.row_token.astype(np.int32)).cuda(),
-                             bm=bm_for(r.rows, E),
+                             kernel=nv.nvfp4_kernel_name(r.rows, E, n, k, 1),
                              flops=2 * r.rows * n * k, bytes=grouped_bytes(r.counts, n, k)))
     torch.cuda.synchronize()
     return launches
-
-
-def bm_for(rows, experts):
-    # mirrors the library's row-tile choice for grouped launches (for naming
-    # the kernel instantiation in the roofline record)
-    avg = (rows + experts - 1) // experts
-    bm = 16 if avg <= 16 else (32 if avg <= 32 else 64)
-    if 8 < avg <= 24:
-        bm = 32
-    return bm
-
-
-def kernel_for(bm):
-    # mirrors the library's kernel configuration for K % 64 == 0: 4-wave
-    # workgroups on 128-column tiles up to 32 rows, 8 waves on 256 columns
-    # for 64-row tiles (template arguments: rows, ring slots, waves, columns,
-    # rows gathered through an index)
-    if bm == 16:
-        return "nvfp4::gemm_kp_kernel<16, 5, 4, 128, false>"
-    if bm == 32:
-        return "nvfp4::gemm_kp_kernel<32, 4, 4, 128, false>"
-    return "nvfp4::gemm_kp_kernel<64, 4, 8, 256, false>"
 
 
 def run_launch(L):
@@ -160,9 +139,44 @@ def traffic_record(kernel_name):
     return ent.get("bytes_per_launch")
 
 
+_SINGLE_THREAD_SCRIPT = r"""
+import json, sys, time
+sys.path.insert(0, "@ROOT@")
+import oracle, workloads as W
+out = {}
+def timed(fn, min_s=0.3):
+    n, t0 = 0, time.perf_counter()
+    while True:
+        fn(); n += 1
+        el = time.perf_counter() - t0
+        if el >= min_s:
+            return el / n
+x, w = W.small_dense()
+t = timed(lambda: oracle.quantize(w))
+p, s, g = oracle.quantize(w)
+out["small_dense_16x256x512"] = {
+    "quantize_GBps": w.nbytes / t / 1e9,
+    "gemm_GFLOPS": 2 * 16 * 256 * 512 / timed(lambda: oracle.gemm(x, p, s, g[0])) / 1e9}
+w = W.decode_weight()
+t0 = time.perf_counter(); p, s, g = oracle.quantize(w); tq = time.perf_counter() - t0
+d = {"quantize_GBps": w.nbytes / tq / 1e9,
+     "gemm_sample": "the first 128 of the 4096 weight rows (output columns)"}
+for m in (1, 16, 64):
+    x = W.decode_act(m)
+    d["gemm_m%d_GFLOPS" % m] = 2 * m * 128 * 7168 / timed(
+        lambda: oracle.gemm(x, p[:128], s[:128], g[0]), 0.2) / 1e9
+out["decode_4096x7168"] = d
+print(json.dumps(out))
+"""
+
+
 def cpu_baseline(min_seconds):
     """The CPU oracle (plain C, OpenMP over rows) on whole expert segments of
-    launch 1 until at least `min_seconds` of wall time have been spent."""
+    launch 1 until at least `min_seconds` of wall time have been spent, its
+    quantize on the same experts' weights, and -- in a child process with one
+    OpenMP thread -- the small dense product and the decode sweep (quantize
+    and M = 1 / 16 / 64 at N = 4096, K = 7168)."""
+    import subprocess
     import numpy as np
     import oracle
     import workloads as W
@@ -171,6 +185,8 @@ def cpu_baseline(min_seconds):
     n, k = 4096, 6144
     flops = 0
     elapsed = 0.0
+    q_elapsed = 0.0
+    q_bytes = 0
     experts = 0
     rows = 0
     for e in range(r.num_experts):
@@ -179,7 +195,10 @@ def cpu_baseline(min_seconds):
             continue
         w = W.normal_bf16((1, n, k), 0.02, (W.SEED, W.W_MOE_UNIFORM, W.S_WEIGHT, 500 + e))
         x = W.normal_bf16((c, k), 1.0, (W.SEED, W.W_MOE_UNIFORM, W.S_ACT, 500 + e))
+        t0 = time.perf_counter()
         p, s, g = oracle.quantize(w)
+        q_elapsed += time.perf_counter() - t0
+        q_bytes += w.nbytes
         off = np.array([0, c], np.int32)
         t0 = time.perf_counter()
         oracle.grouped_gemm(x, off, p, s, g)
@@ -190,11 +209,26 @@ def cpu_baseline(min_seconds):
         if elapsed >= min_seconds:
             break
     threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count()
-    return {"value": flops / elapsed / 1e12, "unit": "TFLOPS", "cores": threads,
-            "kind": "oracle",
-            "sample": "%d experts (%d rows) of the ~16 tok/expert up projection "
-                      "(N=4096, K=6144), FP64-accumulate oracle GEMM, %.1f s" %
-                      (experts, rows, elapsed)}
+    res = {"value": flops / elapsed / 1e12, "unit": "TFLOPS", "cores": threads,
+           "kind": "oracle",
+           "sample": "%d experts (%d rows) of the ~16 tok/expert up projection "
+                     "(N=4096, K=6144), FP64-accumulate oracle GEMM, %.1f s" %
+                     (experts, rows, elapsed),
+           "quantize": {"GBps": q_bytes / q_elapsed / 1e9, "cores": threads,
+                        "sample": "the same %d experts' 4096 x 6144 BF16 weights, %.1f s" %
+                                  (experts, q_elapsed)}}
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    t0 = time.perf_counter()
+    out = subprocess.run([sys.executable, "-c", _SINGLE_THREAD_SCRIPT.replace("@ROOT@", ROOT)], env=env,
+                         capture_output=True, text=True, timeout=600)
+    if out.returncode == 0:
+        st = json.loads(out.stdout.strip().splitlines()[-1])
+        st["cores"] = 1
+        st["seconds"] = time.perf_counter() - t0
+        res["single_thread"] = st
+    else:
+        res["single_thread"] = {"error": out.stderr[-500:]}
+    return res
 
 
 def time_fn(fn, iters, warm):
@@ -390,6 +424,51 @@ def combine_extras(launches):
     return out
 
 
+def moe_layer_extras(launches):
+    """A whole routed MoE layer at ~64 tok/expert (Zipf): gather + gate_up with
+    the SiLU(gate) * up epilogue (N = 4096 fused, K = 6144) -> down projection
+    (N = 6144, K = 2048) -> router-weighted combine of each token's 8 rows,
+    timed as eager launches and as one captured HIP graph replayed."""
+    import torch
+    import block_scaled_fp4_nibble_amd as nv
+    import workloads as W
+
+    up = next(L for L in launches if L["name"] == "up_zipf_64tpe")
+    down = next(L for L in launches if L["name"] == "down_zipf_64tpe")
+    r = W.moe_zipf_routing()
+    x_tok = randn_bf16((r.tokens, up["k"]), 1.0, 700)
+    tr = torch.from_numpy(r.token_rows()).cuda()
+    wts = torch.rand((r.tokens, r.topk), generator=torch.Generator("cuda").manual_seed(701),
+                     device="cuda")
+    h = torch.empty((r.rows, up["n"] // 2), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((r.rows, down["n"]), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((r.tokens, down["n"]), dtype=torch.bfloat16, device="cuda")
+
+    def layer():
+        nv.grouped_gemm_gather(x_tok, up["row_token"], up["off"], up["qw"], act="swiglu", out=h)
+        nv.grouped_gemm(h, down["off"], down["qw"], out=y)
+        nv.moe_combine(y, tr, wts, out=out)
+    layer()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        layer()
+    ms_e = ms_g = float("inf")
+    for _ in range(2):
+        ms_e = min(ms_e, time_fn(layer, 20, 3))
+        ms_g = min(ms_g, time_fn(g.replay, 20, 3))
+    flops = 2 * r.rows * up["n"] * up["k"] + 2 * r.rows * down["n"] * down["k"]
+    return {"moe_layer_zipf_64tpe": {"eager_us": ms_e * 1e3, "graph_us": ms_g * 1e3,
+                                     "TFLOPS_graph": flops / (ms_g * 1e-3) / 1e12,
+                                     "tokens": r.tokens, "topk": r.topk}}
+
+
 def w4a4_extras(launches):
     """The ~16 tok/expert up launch with NVFP4 activations: quantizing the
     activations, then the W4A4 launch (decode of the activations included),
@@ -530,16 +609,16 @@ def main():
         v = sorted(v)
         return v[min(len(v) - 1, int(round(q * (len(v) - 1))))]
 
-    # dominant kernel instantiation by total time
-    by_bm = {}
+    # dominant kernel instantiation by total time (the library names the
+    # kernel each launch runs)
+    by_kernel = {}
     for L, ms in zip(launches, launch_ms):
-        d = by_bm.setdefault(L["bm"], {"ms": 0.0, "bytes": 0, "launches": 0, "names": []})
+        d = by_kernel.setdefault(L["kernel"], {"ms": 0.0, "bytes": 0, "launches": 0, "names": []})
         d["ms"] += ms
         d["bytes"] += L["bytes"]
         d["launches"] += 1
         d["names"].append(L["name"])
-    bm, dom = max(by_bm.items(), key=lambda kv: kv[1]["ms"])
-    kernel = kernel_for(bm)
+    kernel, dom = max(by_kernel.items(), key=lambda kv: kv[1]["ms"])
     avg_ms = dom["ms"] / dom["launches"]
     bytes_per_launch = dom["bytes"] / dom["launches"]
     achieved = bytes_per_launch / (avg_ms * 1e-3) / 1e9
@@ -592,6 +671,7 @@ def main():
         ex.update(gather_extras(launches))
         ex.update(combine_extras(launches))
         ex.update(w4a4_extras(launches))
+        ex.update(moe_layer_extras(launches))
         ex.update(extras())
         # the same rates against what this box measured (context for the
         # spec peaks): the dominant kernel's algorithmic GB/s over a device

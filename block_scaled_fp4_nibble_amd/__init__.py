@@ -39,6 +39,7 @@ EXPORTED = [
     "nvfp4_quantize_workspace_size",
     "nvfp4_gemm_workspace_size", "nvfp4_grouped_gemm_workspace_size",
     "nvfp4_workspace_counter_bytes", "nvfp4_workspace_init", "nvfp4_status_string",
+    "nvfp4_kernel_name",
     "nvfp4_version",
 ]
 
@@ -99,6 +100,8 @@ def load_library(path: str = LIB_PATH):
         lib.nvfp4_workspace_counter_bytes.restype = SZ
         lib.nvfp4_workspace_init.argtypes = [P, SZ, P]
         lib.nvfp4_workspace_init.restype = I32
+        lib.nvfp4_kernel_name.argtypes = [I64, I64, I64, I64, I32, I32]
+        lib.nvfp4_kernel_name.restype = ctypes.c_char_p
         lib.nvfp4_status_string.argtypes = [I32]
         lib.nvfp4_status_string.restype = ctypes.c_char_p
         lib.nvfp4_version.argtypes = []
@@ -225,6 +228,11 @@ def nvfp4_workspace_counter_bytes() -> int:
 
 def nvfp4_workspace_init(workspace, ws_bytes, stream=None):
     return load_library().nvfp4_workspace_init(_ptr(workspace), ws_bytes, _stream(stream))
+
+
+def nvfp4_kernel_name(rows, num_experts, n, k, grouped, gather=0) -> str:
+    return load_library().nvfp4_kernel_name(rows, num_experts, n, k, int(grouped),
+                                            int(gather)).decode()
 
 
 def nvfp4_status_string(status: int) -> str:

@@ -137,6 +137,14 @@ size_t nvfp4_grouped_gemm_workspace_size(int64_t rows, int64_t num_experts, int6
   return nvfp4::plan_gemm(rows, num_experts, n, k, true, cu_count()).ws_bytes;
 }
 
+const char* nvfp4_kernel_name(int64_t rows, int64_t num_experts, int64_t n, int64_t k,
+                              int32_t grouped, int32_t gather) {
+  if (rows <= 0 || num_experts <= 0 || n <= 0 || check_k(k) != NVFP4_OK) return "";
+  const nvfp4::GemmPlan pl =
+      nvfp4::plan_gemm(rows, num_experts, n, k, grouped != 0, cu_count());
+  return nvfp4::plan_kernel_name(pl, grouped != 0 && gather != 0);
+}
+
 static nvfp4_status_t run_gemm(const void* x, int64_t rows, const int32_t* offsets, int64_t E,
                                int64_t n, int64_t k, const uint8_t* packed,
                                const uint8_t* scales, const float* g, void* y, nvfp4_out_t out,

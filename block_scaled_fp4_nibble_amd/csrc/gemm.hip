@@ -1746,6 +1746,43 @@ bool plan_pairs_tiles(const GemmPlan& pl) {
   return pl.kind == 0 || pl.kind == 1 || pl.kind == 2;
 }
 
+// Name of the kernel instantiation launch_gemm runs for a plan (as profilers
+// print it), for tooling that reports per-kernel figures.
+const char* plan_kernel_name(const GemmPlan& pl, bool gather) {
+  if (pl.kind == 6) {
+    static const char* kGemv[] = {"nvfp4::gemv_kernel<1>", "nvfp4::gemv_kernel<2>",
+                                  "nvfp4::gemv_kernel<3>", "nvfp4::gemv_kernel<4>"};
+    return kGemv[std::min(std::max(pl.bm, 1), 4) - 1];
+  }
+  if (pl.kind == 7) {
+    // the template argument is the number of 128-deep K groups per wave
+    static const char* kDec[] = {"nvfp4::decode_mfma_kernel<1>", "nvfp4::decode_mfma_kernel<2>",
+                                 "nvfp4::decode_mfma_kernel<3>", "nvfp4::decode_mfma_kernel<4>",
+                                 "nvfp4::decode_mfma_kernel<5>", "nvfp4::decode_mfma_kernel<6>",
+                                 "nvfp4::decode_mfma_kernel<7>", "nvfp4::decode_mfma_kernel<8>"};
+    const int per_wave = (pl.k_split / 128 + kGemvWaves - 1) / kGemvWaves;
+    return kDec[std::min(std::max(per_wave, 1), 8) - 1];
+  }
+  if (pl.kind == 3) return "nvfp4::gemm_lm_kernel";
+#define NVFP4_KP_NAME(BM, NS, KW, BN) \
+  return gather ? "nvfp4::gemm_kp_kernel<" #BM ", " #NS ", " #KW ", " #BN ", true>" \
+                : "nvfp4::gemm_kp_kernel<" #BM ", " #NS ", " #KW ", " #BN ", false>"
+  if (pl.kind == 1) {
+    if (pl.bm == 16) NVFP4_KP_NAME(16, 5, 4, 128);
+    NVFP4_KP_NAME(32, 4, 4, 128);
+  }
+  if (pl.kind == 4) NVFP4_KP_NAME(16, 5, 4, 64);
+  if (pl.kind == 2) {
+    if (pl.bm == 16) NVFP4_KP_NAME(16, 5, 8, 256);
+    if (pl.bm == 32) NVFP4_KP_NAME(32, 5, 8, 256);
+    NVFP4_KP_NAME(64, 4, 8, 256);
+  }
+#undef NVFP4_KP_NAME
+  if (pl.bm == 16) return "nvfp4::gemm_reg_kernel<16>";
+  if (pl.bm == 32) return "nvfp4::gemm_reg_kernel<32>";
+  return "nvfp4::gemm_reg_kernel<64>";
+}
+
 hipError_t launch_gemm(const GemmPlan& pl, const GemmParams& p, hipStream_t stream) {
   if (pl.kind == 6 || pl.kind == 7) return launch_gemv(pl, p, stream);
   dim3 grid(pl.grid);

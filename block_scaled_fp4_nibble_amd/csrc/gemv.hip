@@ -28,8 +28,6 @@ namespace nvfp4 {
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 
-constexpr int kGemvThreads = 512;  // 8 waves
-constexpr int kGemvWaves = kGemvThreads / kWave;
 constexpr int kGemvCols = 16;      // weight rows (output columns) per workgroup
 constexpr int kGemvBatch = 8;      // chunks a lane loads before it multiplies them
 

@@ -63,11 +63,15 @@ struct GemmPlan {
 // dot-product kernel (gemv.hip), which stages the rows in LDS (at most
 // kGemvMaxXBytes).
 constexpr int kGemvMaxRows = 4;
+// Both decode kernels run 8-wave workgroups.
+constexpr int kGemvThreads = 512;
+constexpr int kGemvWaves = kGemvThreads / 64;
 constexpr int64_t kGemvMaxXBytes = 65536;
 
 GemmPlan plan_gemm(int64_t rows, int64_t num_experts, int64_t n, int64_t k, bool grouped,
                    int cu_count);
 hipError_t launch_gemm(const GemmPlan& plan, const GemmParams& p, hipStream_t stream);
+const char* plan_kernel_name(const GemmPlan& plan, bool gather);
 hipError_t launch_gemv(const GemmPlan& plan, const GemmParams& p, hipStream_t stream);
 // True when every wave of the planned kernel ends with an even number of
 // 16-column tiles (what the SiLU(gate) * up epilogue needs).

@@ -261,6 +261,16 @@ size_t nvfp4_quantize_workspace_size(int64_t batch, int64_t n, int64_t k);
 size_t nvfp4_gemm_workspace_size(int64_t m, int64_t n, int64_t k);
 size_t nvfp4_grouped_gemm_workspace_size(int64_t rows, int64_t num_experts, int64_t n,
                                          int64_t k);
+/* Name of the kernel instantiation (as profilers print it, e.g.
+ * "nvfp4::gemm_kp_kernel<64, 4, 8, 256, false>") that nvfp4_gemm (grouped = 0,
+ * num_experts = 1) or nvfp4_grouped_gemm / _swiglu (grouped = 1; gather = 1:
+ * nvfp4_grouped_gemm_gather) launches for this shape on the current device,
+ * under the current tuning environment.  Static string; "" for an invalid
+ * shape.  For reporting (per-kernel profiles, rooflines); it enqueues
+ * nothing. */
+const char* nvfp4_kernel_name(int64_t rows, int64_t num_experts, int64_t n, int64_t k,
+                              int32_t grouped, int32_t gather);
+
 /* Bytes at the start of any workspace that hold tile counters. */
 size_t nvfp4_workspace_counter_bytes(void);
 

@@ -1580,6 +1580,12 @@ static int env_int(const char* name, int dflt) {
 //      with NVFP4_KPCFG=8)
 //   3  large-M kernel, 256 x 256 tiles (dense products with at least
 //      kLmMinRows rows; NVFP4_LM=0 disables it)
+//   4  K-phase kernel, 4 waves x 64 columns (dense, up to 16 rows)
+//   6  dot-product kernel (dense, one to four rows; gemv.hip)
+//   7  one MFMA row tile per 16 columns, whole K (dense, 5 to 16 rows with
+//      NVFP4_DSK=0; gemv.hip)
+//   8  split-K decode kernel, 64 columns per unit (dense, 17 to 64 rows, or
+//      5 to 64 with NVFP4_DSK=2; NVFP4_DSK=0 disables it; gemv.hip)
 constexpr int kLmMinRows = 256;
 constexpr int kMinSplitStages = 7;
 
@@ -1662,6 +1668,34 @@ GemmPlan plan_gemm(int64_t rows, int64_t num_experts, int64_t n, int64_t k, bool
     pl.dyn_lds = (int)(rows * k * 2);
     pl.ws_bytes = 0;
     return pl;
+  }
+  // five to sixty-four dense rows, k % 128 == 0: split-K decode kernel, 64
+  // columns per unit, each workgroup's weight share in flight at once (kind
+  // 8, gemv.hip); the split count about fills the CUs with units
+  const int dsk = env_int("NVFP4_DSK", 1);
+  if (!grouped && rows > kGemvMaxRows && rows <= 64 && k % 128 == 0 &&
+      env_int("NVFP4_GEMV", 1) != 0 && (dsk == 2 || (dsk == 1 && rows > 16))) {
+    const int64_t n_tiles = (n + kDskCols - 1) / kDskCols;
+    const int64_t groups = k / 128;
+    int64_t splits = std::min<int64_t>(groups, std::max<int64_t>(1, cu_count / n_tiles));
+    splits = std::max<int64_t>(splits, (groups + kDskMaxGroups - 1) / kDskMaxGroups);
+    const int64_t kgroups = (groups + splits - 1) / splits;
+    splits = (groups + kgroups - 1) / kgroups;
+    if (splits == 1 || n_tiles <= kMaxCounters) {
+      pl.kind = 8;
+      pl.bm = (int)((rows + 15) / 16 * 16);
+      pl.bn = kDskCols;
+      pl.splits = (int)splits;
+      pl.k_split = (int)(kgroups * 128);
+      pl.n_tiles = (int)n_tiles;
+      pl.max_tiles = pl.n_tiles;
+      pl.grid = (int)(splits * n_tiles);
+      pl.dyn_lds = 0;
+      pl.ws_bytes = splits > 1 ? kCounterBytes + (size_t)n_tiles * splits * pl.bm * kDskCols *
+                                                     sizeof(float)
+                               : 0;
+      return pl;
+    }
   }
   // five to sixteen dense rows, k % 128 == 0: one MFMA row tile per 16
   // columns, whole K, every load in flight at once (kind 7, gemv.hip)
@@ -1763,6 +1797,11 @@ const char* plan_kernel_name(const GemmPlan& pl, bool gather) {
     const int per_wave = (pl.k_split / 128 + kGemvWaves - 1) / kGemvWaves;
     return kDec[std::min(std::max(per_wave, 1), 8) - 1];
   }
+  if (pl.kind == 8) {
+    static const char* kDsk[] = {"nvfp4::decode_sk_kernel<1>", "nvfp4::decode_sk_kernel<2>",
+                                 "nvfp4::decode_sk_kernel<3>", "nvfp4::decode_sk_kernel<4>"};
+    return kDsk[std::min(std::max(pl.bm / 16, 1), 4) - 1];
+  }
   if (pl.kind == 3) return "nvfp4::gemm_lm_kernel";
 #define NVFP4_KP_NAME(BM, NS, KW, BN) \
   return gather ? "nvfp4::gemm_kp_kernel<" #BM ", " #NS ", " #KW ", " #BN ", true>" \
@@ -1784,7 +1823,7 @@ const char* plan_kernel_name(const GemmPlan& pl, bool gather) {
 }
 
 hipError_t launch_gemm(const GemmPlan& pl, const GemmParams& p, hipStream_t stream) {
-  if (pl.kind == 6 || pl.kind == 7) return launch_gemv(pl, p, stream);
+  if (pl.kind == 6 || pl.kind == 7 || pl.kind == 8) return launch_gemv(pl, p, stream);
   dim3 grid(pl.grid);
 #define NVFP4_KP(BM, NS, KW, BN)                                                           \
   do {                                                                                     \

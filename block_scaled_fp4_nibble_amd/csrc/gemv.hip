@@ -238,7 +238,319 @@ __global__ __launch_bounds__(kGemvThreads) void decode_mfma_kernel(GemmParams p)
   }
 }
 
+// ---- 5 to 64 rows: split K, a workgroup's whole weight share in flight --------
+//
+// Decode moves each weight byte once, and with a few dozen rows the per-CU
+// weight share is a few tens of KB: the time is about one HBM latency plus
+// the transfer, provided every load of the share is in flight from the start.
+// The K-phase kernel's ring keeps only a few 128-deep stages in flight, and
+// decode_mfma_kernel reads the token rows once per 16 columns (at 64 rows the
+// activations would outweigh the weights 16:1).  Here a unit is 64 output
+// columns x one K split (k_split, at most 16 groups of 128), with the split
+// count chosen so that the units about fill the CUs (N = 4096, K = 7168: 64
+// column tiles x 4 splits).  Wave w of the 8 owns the unit's 128-deep K groups
+// j with j % 8 == w, for all four 16-column tiles, so every activation
+// fragment it reads from LDS feeds four MFMAs.  Each lane first loads the
+// first phase of the token rows, then issues every weight load of its share
+// -- per group and column tile 16 bytes of its weight row at K = 128 j +
+// 32 (l / 16) and the two scale bytes, the K-slot permutation of
+// decode_mfma_kernel.  The token rows (split K range, all rows) go through
+// registers into LDS in phases of up to kDskPhase<NF> groups, each row's
+// 16-byte chunk c at c ^ (row % 16); with up to 32 rows the next phase's
+// loads are in flight while this phase is multiplied out.  The waves' sums meet through LDS in a
+// fixed order, the splits of a column tile through device-scope partial tiles
+// and an arrival counter, and the last split sums them in split order (so the
+// result does not depend on timing).
+constexpr int kDskXBytes = 120 * 1024;  // LDS for one phase of token rows
+template <int NF>
+constexpr int kDskPhase = (kDskXBytes / (NF * 16 * 256)) < kDskMaxGroups ? kDskXBytes / (NF * 16 * 256)
+                                                                           : kDskMaxGroups;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dsk_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+// device-scope (sc1) buffer accesses: past the non-coherent L2
+constexpr int kDskCpol = 16;
+constexpr uint32_t kDskOffNone = 0x80000000u;  // beyond every resource: loads return 0
+
+template <int NF>
+__global__ __launch_bounds__(kGemvThreads) void decode_sk_kernel(GemmParams p) {
+  constexpr int BM = NF * 16;
+  constexpr int CT = kDskCols / 16;                  // column tiles per unit
+  constexpr int PG = kDskPhase<NF>;                  // groups per token-row phase
+  constexpr int RCH = PG * 16;                       // 16-byte chunks per staged row
+  constexpr int CPT = (BM * RCH + kGemvThreads - 1) / kGemvThreads;  // chunks per thread
+  constexpr int GPW = kDskMaxGroups / kGemvWaves;    // groups per wave (upper bound)
+  constexpr int NPH = (kDskMaxGroups + PG - 1) / PG; // phases (upper bound)
+  constexpr bool kPrefetch = NF <= 2;
+  static_assert(kDskCols % 16 == 0 && kDskMaxGroups % kGemvWaves == 0, "unit shape");
+  static_assert((kGemvWaves / 2) * NF * CT * 16 * kWave <= BM * RCH * 16, "exchange fits");
+  __shared__ __attribute__((aligned(16))) uint8_t xs[BM * RCH * 16];
+  __shared__ int last_flag;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c16 = lane & 15, g = lane >> 4;
+  const int K = p.k, N = p.n, M = (int)p.rows;
+  // unit: XCD-major placement (workgroup b runs on XCD b % 8), so the column
+  // tiles of one split -- which read the same token-row range -- share an L2
+  const int G = gridDim.x, b = blockIdx.x;
+  const int v = (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
+  const int s = v / p.n_tiles, nt = v % p.n_tiles;
+  const int k0 = s * p.k_split;
+  const int ng = (min(K, k0 + p.k_split) - k0) / 128;  // K groups of this unit
+  const int nrows = min(kDskCols, N - nt * kDskCols);  // weight rows of the unit
+  // buffer resources: loads past a resource (rows past N, rows past M, K
+  // groups past the unit) read zero, so no load sits behind a branch
+  const __amdgpu_buffer_rsrc_t rx = dsk_rsrc(p.x, (uint32_t)M * (uint32_t)K * 2u);
+  const __amdgpu_buffer_rsrc_t rw =
+      dsk_rsrc(p.w + (int64_t)nt * kDskCols * (K / 2), (uint32_t)(nrows * (K / 2)));
+  const __amdgpu_buffer_rsrc_t rs =
+      dsk_rsrc(p.s + (int64_t)nt * kDskCols * (K / 16), (uint32_t)(nrows * (K / 16)));
+
+  // token rows of phase `ph` (groups [ph PG, min(ng, ph PG + PG))) into xr
+  u32x4_t xr[CPT];
+  auto load_phase = [&](int ph) {
+    const int gb = ph * PG;
+    const int rc = (min(ng, gb + PG) - gb) * 16;  // chunks per row in this phase
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int ci = tid + i * kGemvThreads;
+      const int row = ci / RCH, c = ci % RCH;
+      const bool ok = row < M && c < rc && ci < BM * RCH;
+      const uint32_t off =
+          ok ? ((uint32_t)row * (uint32_t)K + (uint32_t)(k0 + gb * 128 + 8 * c)) * 2u : kDskOffNone;
+      xr[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
+    }
+  };
+  auto store_phase = [&]() {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int ci = tid + i * kGemvThreads;
+      if (ci < BM * RCH) {
+        const int row = ci / RCH, c = ci % RCH;
+        *reinterpret_cast<u32x4_t*>(xs + (row * RCH + (c ^ (row & 15))) * 16) = xr[i];
+      }
+    }
+  };
+
+  // the first token rows go out before the weights (a scheduling fence: no
+  // memory fence, which would make the compiler wait for the loads)
+  load_phase(0);
+  __builtin_amdgcn_sched_barrier(0);
+  u32x4_t wv[GPW][CT];
+  uint32_t sv[GPW][CT];
+#pragma unroll
+  for (int i = 0; i < GPW; ++i) {
+    const int j = wave + kGemvWaves * i;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const int r = 16 * ct + c16;  // weight row within the unit
+      const bool ok = j < ng;
+      const uint32_t wo = ok ? (uint32_t)(r * (K / 2) + (k0 + 128 * j) / 2 + 16 * g) : kDskOffNone;
+      const uint32_t so = ok ? (uint32_t)(r * (K / 16) + (k0 + 128 * j) / 16 + 2 * g) : kDskOffNone;
+      wv[i][ct] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, wo, 0, 0));
+      sv[i][ct] = __builtin_amdgcn_raw_buffer_load_b16(rs, so, 0, 0);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  store_phase();
+  __syncthreads();
+
+  f32x4_t acc[NF][CT];
+#pragma unroll
+  for (int f = 0; f < NF; ++f)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) acc[f][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ph = 0; ph < NPH; ++ph) {
+    const int gb = ph * PG;
+    if (gb >= ng) break;  // uniform
+    const bool more = gb + PG < ng;
+    // the next phase's rows are in flight while this one is multiplied out
+    // (with up to 32 rows; above that the registers would not hold them)
+    if (kPrefetch && more) load_phase(ph + 1);
+#pragma unroll
+    for (int i = 0; i < GPW; ++i) {
+      const int j = wave + kGemvWaves * i;
+      if (j < gb || j >= gb + PG || j >= ng) continue;  // wave-uniform
+      const int jj = j - gb;
+      // A fragments of step t + 1 are read while step t is dequantized and
+      // multiplied (LDS latency behind the MFMAs)
+      bf16x8_t a[2][NF];
+      auto read_a = [&](bf16x8_t (&dst)[NF], int t) {
+        const int c = 16 * jj + 4 * g + t;  // K = 128 j + 32 g + 8 t .. + 7
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          const int row = 16 * f + c16;
+          dst[f] = *reinterpret_cast<const bf16x8_t*>(xs + (row * RCH + (c ^ (row & 15))) * 16);
+        }
+      };
+      read_a(a[0], 0);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        if (t < 3) read_a(a[(t + 1) & 1], t + 1);
+        bf16x8_t bq[CT];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          const float sc = t < 2 ? decode_e4m3<0>(sv[i][ct]) : decode_e4m3<1>(sv[i][ct]);
+          bq[ct] = dequant8(wv[i][ct][t], sc);
+        }
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct)
+            acc[f][ct] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[t & 1][f], bq[ct], acc[f][ct], 0, 0, 0);
+      }
+    }
+    if (more) {
+      __syncthreads();  // every wave is done with this phase's rows
+      if (!kPrefetch) load_phase(ph + 1);
+      store_phase();
+      __syncthreads();
+    }
+  }
+
+  // sum the waves in a fixed order: w += w + 4 (w < 4), then wave 0 adds
+  // waves 1, 2, 3
+  f32x4_t* xch = reinterpret_cast<f32x4_t*>(xs);
+  auto put = [&](int slot) {
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) xch[((slot * NF + f) * CT + ct) * kWave + lane] = acc[f][ct];
+  };
+  auto add = [&](int slot) {
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+        acc[f][ct] = acc[f][ct] + xch[((slot * NF + f) * CT + ct) * kWave + lane];
+  };
+  __syncthreads();
+  if (wave >= 4) put(wave - 4);
+  __syncthreads();
+  if (wave < 4) add(wave);
+  __syncthreads();
+  if (wave >= 1 && wave < 4) put(wave);
+  __syncthreads();
+  if (wave == 0) {
+    add(1);
+    add(2);
+    add(3);
+  }
+  const int S = p.splits;
+  if (S > 1) {
+    const __amdgpu_buffer_rsrc_t part =
+        dsk_rsrc(p.partials + (int64_t)nt * S * (BM * kDskCols), (uint32_t)(S * BM * kDskCols * 4));
+    auto poff = [&](int ss, int f, int ct) {
+      return (uint32_t)((ss * (BM * kDskCols) + ((f * CT + ct) * kWave + lane) * 4) * 4);
+    };
+    if (wave == 0) {
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, acc[f][ct]), part,
+                                                 poff(s, f, ct), 0, kDskCpol);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // the partial stores have completed
+    __syncthreads();
+    if (tid == 0) {
+      const uint32_t old =
+          __hip_atomic_fetch_add(&p.counters[nt], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last_flag = old == (uint32_t)(S - 1);
+    }
+    __syncthreads();
+    if (!last_flag) return;  // uniform: another split finishes the tile
+    if (wave == 0) {
+      f32x4_t sum[NF][CT];
+      for (int ss = 0; ss < S; ++ss) {
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            const f32x4_t vv =
+                ss == s ? acc[f][ct]
+                        : __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                          part, poff(ss, f, ct), 0, kDskCpol));
+            sum[f][ct] = ss == 0 ? vv : sum[f][ct] + vv;
+          }
+      }
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) acc[f][ct] = sum[f][ct];
+    }
+    if (tid == 0) __hip_atomic_store(&p.counters[nt], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // Output: wave 0 lays the tile out row-major in LDS (FP32, g applied), then
+  // every thread writes whole 16-byte pieces of the tile's rows -- one store
+  // per piece instead of one 2- or 4-byte store per element -- and only the
+  // pieces that reach past column N, or whose rows are not 16-byte aligned,
+  // go element by element.
+  float* tile = reinterpret_cast<float*>(xs);  // [BM][kDskCols]
+  __syncthreads();  // the exchange slots are free
+  if (wave == 0) {
+    const float gv = p.g[0];
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          tile[(16 * f + 4 * g + r) * kDskCols + 16 * ct + c16] = gv * acc[f][ct][r];
+  }
+  __syncthreads();
+  const int esz = p.out_f32 ? 4 : 2;
+  const int cpr = kDskCols * esz / 16;  // 16-byte pieces per tile row
+  const int ncol0 = nt * kDskCols;
+  const bool rows_aligned = (N * esz) % 16 == 0;
+  const __amdgpu_buffer_rsrc_t ry = dsk_rsrc(p.y, (uint32_t)M * (uint32_t)N * (uint32_t)esz);
+  for (int q = tid; q < BM * cpr; q += kGemvThreads) {
+    const int row = q / cpr, piece = q % cpr;
+    if (row >= M) continue;
+    const int per = 16 / esz;                // elements per piece
+    const int col = ncol0 + piece * per;     // first column of the piece
+    const float* src = tile + row * kDskCols + piece * per;
+    const uint32_t base = ((uint32_t)row * (uint32_t)N + (uint32_t)col) * (uint32_t)esz;
+    if (rows_aligned && col + per <= N) {
+      u32x4_t v;
+      if (p.out_f32) {
+        v = u32x4_t{__float_as_uint(src[0]), __float_as_uint(src[1]), __float_as_uint(src[2]),
+                    __float_as_uint(src[3])};
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          v[e] = float_to_bf16_rne(src[2 * e]) | (float_to_bf16_rne(src[2 * e + 1]) << 16);
+      }
+      __builtin_amdgcn_raw_buffer_store_b128(v, ry, base, 0, 0);
+    } else {
+      for (int e = 0; e < per; ++e) {
+        if (col + e >= N) break;
+        if (p.out_f32)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(src[e]), ry, base + 4u * e, 0, 0);
+        else
+          __builtin_amdgcn_raw_buffer_store_b16((uint16_t)float_to_bf16_rne(src[e]), ry,
+                                                base + 2u * e, 0, 0);
+      }
+    }
+  }
+}
+
 hipError_t launch_gemv(const GemmPlan& pl, const GemmParams& p, hipStream_t stream) {
+  if (pl.kind == 8) {
+    const dim3 grid((unsigned)pl.grid), block(kGemvThreads);
+    switch (pl.bm) {
+      case 16: hipLaunchKernelGGL(decode_sk_kernel<1>, grid, block, 0, stream, p); break;
+      case 32: hipLaunchKernelGGL(decode_sk_kernel<2>, grid, block, 0, stream, p); break;
+      case 48: hipLaunchKernelGGL(decode_sk_kernel<3>, grid, block, 0, stream, p); break;
+      case 64: hipLaunchKernelGGL(decode_sk_kernel<4>, grid, block, 0, stream, p); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   if (pl.kind == 7) {
     const dim3 grid((unsigned)pl.grid), block(kGemvThreads);
     const int per_wave = (p.k / 128 + kGemvWaves - 1) / kGemvWaves;  // K groups per wave

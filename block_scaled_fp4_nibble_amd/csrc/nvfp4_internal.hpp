@@ -67,6 +67,11 @@ constexpr int kGemvMaxRows = 4;
 constexpr int kGemvThreads = 512;
 constexpr int kGemvWaves = kGemvThreads / 64;
 constexpr int64_t kGemvMaxXBytes = 65536;
+// Dense products of 5 to 64 rows with k % 128 == 0 run on the split-K decode
+// kernel (gemv.hip): units of kDskCols output columns by at most
+// kDskMaxGroups 128-deep K groups.
+constexpr int kDskCols = 64;
+constexpr int kDskMaxGroups = 16;
 
 GemmPlan plan_gemm(int64_t rows, int64_t num_experts, int64_t n, int64_t k, bool grouped,
                    int cu_count);

@@ -1,4 +1,7 @@
-// gemv.hip -- dense products with one to four token rows (decode).
+// gemv.hip -- dense decode products: one to four token rows (gemv_kernel),
+// 5 to 12 rows (decode_mfma_kernel) and 13 to 64 rows (decode_sk_kernel).
+//
+// One to four rows:
 //
 // Decode is the bandwidth-bound case ("The FP4 Frontier", Finding 7).  With
 // so few rows a 16-row MFMA tile is mostly padding, and the in-register
@@ -19,8 +22,10 @@
 // chunks (32 weights each, 64 contiguous bytes), the waves take the row's
 // next 128-byte groups in turn, so every chunk of the row is read once and
 // each lane keeps up to kGemvBatch chunks in flight.  The token rows are
-// staged in LDS once.  The partial sums are reduced in a fixed order: chunk
-// order within a lane, the four lanes of a row, then the eight waves.
+// staged in LDS once; their loads go out before the weights', so the staging
+// waits for them alone and not for the weight stream behind them.  The
+// partial sums are reduced in a fixed order: chunk order within a lane, the
+// four lanes of a row, then the eight waves.
 #include "nvfp4_internal.hpp"
 #include "device_common.hpp"
 
@@ -31,23 +36,29 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 constexpr int kGemvCols = 16;      // weight rows (output columns) per workgroup
 constexpr int kGemvBatch = 8;      // chunks a lane loads before it multiplies them
 
-// Chunks c0, c0 + STRIDE, ... (kGemvBatch of them) of one weight row: 16
-// packed bytes and two scale bytes each; chunks past the row, and rows past
-// N, read as zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t gemv_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+constexpr uint32_t kGemvOffNone = 0x80000000u;  // beyond every resource: loads return 0
+
+// Chunks c0, c0 + STRIDE, ... (kGemvBatch of them) of weight row r of the
+// workgroup's 16 rows: 16 packed bytes and two scale bytes each.  Buffer
+// loads with no branch: chunks past the row, and rows past N (past the
+// resources), read as zero.
 template <int STRIDE>
 __device__ __forceinline__ void gemv_load_batch(uint4 (&pk)[kGemvBatch], uint32_t (&sc)[kGemvBatch],
-                                                const uint8_t* wrow, const uint8_t* srow, int c0,
-                                                int C, bool row_ok) {
+                                                __amdgpu_buffer_rsrc_t rw,
+                                                __amdgpu_buffer_rsrc_t rs, int r, int K, int c0,
+                                                int C) {
 #pragma unroll
   for (int b = 0; b < kGemvBatch; ++b) {
     const int c = c0 + STRIDE * b;
-    if (row_ok && c < C) {
-      pk[b] = *reinterpret_cast<const uint4*>(wrow + 16 * (int64_t)c);
-      sc[b] = *reinterpret_cast<const uint16_t*>(srow + 2 * (int64_t)c);
-    } else {
-      pk[b] = make_uint4(0u, 0u, 0u, 0u);
-      sc[b] = 0u;
-    }
+    const bool ok = c < C;
+    const uint32_t wo = ok ? (uint32_t)(r * (K / 2) + 16 * c) : kGemvOffNone;
+    const uint32_t so = ok ? (uint32_t)(r * (K / 16) + 2 * c) : kGemvOffNone;
+    pk[b] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, wo, 0, 0));
+    sc[b] = __builtin_amdgcn_raw_buffer_load_b16(rs, so, 0, 0);
   }
 }
 
@@ -59,30 +70,37 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemmParams p) {
   const int K = p.k, N = p.n;
   const int n0 = blockIdx.x * kGemvCols;
   const int r = lane >> 2, cl = lane & 3;
-  const int n = n0 + r;
-  const bool row_ok = n < N;
   const int C = K / 32;  // 32-weight chunks per row
   constexpr int kStride = 4 * kGemvWaves;  // chunks between a lane's consecutive chunks
-  const uint8_t* wrow = p.w + (int64_t)(row_ok ? n : 0) * (K / 2);
-  const uint8_t* srow = p.s + (int64_t)(row_ok ? n : 0) * (K / 16);
+  const int rows16 = min(kGemvCols, N - n0);
+  const __amdgpu_buffer_rsrc_t rw = gemv_rsrc(p.w + (int64_t)n0 * (K / 2), (uint32_t)(rows16 * (K / 2)));
+  const __amdgpu_buffer_rsrc_t rs = gemv_rsrc(p.s + (int64_t)n0 * (K / 16), (uint32_t)(rows16 * (K / 16)));
   uint4 pk[kGemvBatch];
   uint32_t sc[kGemvBatch];
-  // the first weight loads go out before the token rows are staged in LDS
+  // the token rows go out first (registers, then LDS), then the first weight
+  // batch: the staging then waits for the token rows only, not for the
+  // weights behind them
+  constexpr int kXV = (int)(kGemvMaxXBytes / 16 / kGemvThreads);  // 16-byte vectors per thread
+  const int nv = M * K / 8;
+  const __amdgpu_buffer_rsrc_t rx = gemv_rsrc(p.x, (uint32_t)nv * 16u);
+  uint4 xv[kXV];
+#pragma unroll
+  for (int i = 0; i < kXV; ++i) {
+    const int idx = tid + i * kGemvThreads;
+    xv[i] = __builtin_bit_cast(
+        uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, idx < nv ? (uint32_t)idx * 16u : kGemvOffNone,
+                                                     0, 0));
+  }
+  __builtin_amdgcn_sched_barrier(0);
   int c0 = 4 * wave + cl;
-  gemv_load_batch<kStride>(pk, sc, wrow, srow, c0, C, row_ok);
+  gemv_load_batch<kStride>(pk, sc, rw, rs, r, K, c0, C);
+  __builtin_amdgcn_sched_barrier(0);
   {
-    const uint4* src = reinterpret_cast<const uint4*>(p.x);
     uint4* dst = reinterpret_cast<uint4*>(xl);
-    const int nv = M * K / 8;
-    for (int i0 = tid; i0 < nv; i0 += 4 * kGemvThreads) {
-      // four loads in flight (indexes past the end re-read the last vector,
-      // whose store is skipped)
-      uint4 t[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) t[u] = src[min(i0 + u * kGemvThreads, nv - 1)];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (i0 + u * kGemvThreads < nv) dst[i0 + u * kGemvThreads] = t[u];
+    for (int i = 0; i < kXV; ++i) {
+      const int idx = tid + i * kGemvThreads;
+      if (idx < nv) dst[idx] = xv[i];
     }
   }
   __syncthreads();
@@ -124,7 +142,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemmParams p) {
       }
     }
     if (c0 + kStride * kGemvBatch < C)
-      gemv_load_batch<kStride>(pk, sc, wrow, srow, c0 + kStride * kGemvBatch, C, row_ok);
+      gemv_load_batch<kStride>(pk, sc, rw, rs, r, K, c0 + kStride * kGemvBatch, C);
   }
   // the four lanes of a row, then the waves, in a fixed order
 #pragma unroll
@@ -152,7 +170,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemmParams p) {
   }
 }
 
-// ---- 5 to 16 rows: one MFMA row tile, whole K per workgroup -------------------
+// ---- 5 to 12 rows: one MFMA row tile, whole K per workgroup -------------------
 //
 // Above four rows the per-row dot products cost more than one BF16 MFMA row
 // tile, but the K-phase kernel's latency structure (a ring of 128-deep stages,
@@ -238,7 +256,7 @@ __global__ __launch_bounds__(kGemvThreads) void decode_mfma_kernel(GemmParams p)
   }
 }
 
-// ---- 5 to 64 rows: split K, a workgroup's whole weight share in flight --------
+// ---- 13 to 64 rows: split K, a workgroup's whole weight share in flight -------
 //
 // Decode moves each weight byte once, and with a few dozen rows the per-CU
 // weight share is a few tens of KB: the time is about one HBM latency plus

@@ -1,5 +1,5 @@
 // gemv.hip -- dense decode products: one to four token rows (gemv_kernel),
-// 5 to 12 rows (decode_mfma_kernel) and 13 to 64 rows (decode_sk_kernel).
+// 5 to 8 rows (decode_mfma_kernel) and 9 to 64 rows (decode_sk_kernel).
 //
 // One to four rows:
 //
@@ -170,7 +170,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemmParams p) {
   }
 }
 
-// ---- 5 to 12 rows: one MFMA row tile, whole K per workgroup -------------------
+// ---- 5 to 8 rows: one MFMA row tile, whole K per workgroup --------------------
 //
 // Above four rows the per-row dot products cost more than one BF16 MFMA row
 // tile, but the K-phase kernel's latency structure (a ring of 128-deep stages,
@@ -256,7 +256,7 @@ __global__ __launch_bounds__(kGemvThreads) void decode_mfma_kernel(GemmParams p)
   }
 }
 
-// ---- 13 to 64 rows: split K, a workgroup's whole weight share in flight -------
+// ---- 9 to 64 rows: split K, a workgroup's whole weight share in flight --------
 //
 // Decode moves each weight byte once, and with a few dozen rows the per-CU
 // weight share is a few tens of KB: the time is about one HBM latency plus
@@ -482,44 +482,58 @@ __global__ __launch_bounds__(kGemvThreads) void decode_sk_kernel(GemmParams p) {
     }
     __syncthreads();
     if (!last_flag) return;  // uniform: another split finishes the tile
-    if (wave == 0) {
-      f32x4_t sum[NF][CT];
-      for (int ss = 0; ss < S; ++ss) {
+    // The last split sums all S partial tiles (its own included, as stored)
+    // in split order.  The tile's NF x CT accumulator slots are dealt out to
+    // the 8 waves, and each wave issues the loads of up to 8 splits before it
+    // adds any, so the hand-off costs a few memory latencies, not S of them.
+    constexpr int SLOTS = NF * CT;                            // 4 .. 16
+    constexpr int SPW = (SLOTS + kGemvWaves - 1) / kGemvWaves;  // slots per wave
+    constexpr int U = 8;                                      // splits in flight
+    float* tile = reinterpret_cast<float*>(xs);               // [BM][kDskCols]
+    const float gv = p.g[0];
 #pragma unroll
-        for (int f = 0; f < NF; ++f)
+    for (int q = 0; q < SPW; ++q) {
+      const int slot = wave + kGemvWaves * q;
+      if (slot >= SLOTS) break;  // wave-uniform
+      const int f = slot / CT, ct = slot % CT;
+      f32x4_t sum = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int s0 = 0; s0 < S; s0 += U) {
+        f32x4_t v[U];
 #pragma unroll
-          for (int ct = 0; ct < CT; ++ct) {
-            const f32x4_t vv =
-                ss == s ? acc[f][ct]
-                        : __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                          part, poff(ss, f, ct), 0, kDskCpol));
-            sum[f][ct] = ss == 0 ? vv : sum[f][ct] + vv;
-          }
+        for (int i = 0; i < U; ++i)
+          v[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 part, s0 + i < S ? poff(s0 + i, f, ct) : kDskOffNone,
+                                                 0, kDskCpol));
+#pragma unroll
+        for (int i = 0; i < U; ++i)
+          if (s0 + i < S) sum = (s0 + i == 0) ? v[i] : sum + v[i];
       }
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        tile[(16 * f + 4 * g + r) * kDskCols + 16 * ct + c16] = gv * sum[r];
+    }
+    if (tid == 0) __hip_atomic_store(&p.counters[nt], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    // one split: wave 0 holds the whole sum; lay it out row-major in LDS
+    float* tile = reinterpret_cast<float*>(xs);  // [BM][kDskCols]
+    __syncthreads();  // the exchange slots are free
+    if (wave == 0) {
+      const float gv = p.g[0];
 #pragma unroll
       for (int f = 0; f < NF; ++f)
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) acc[f][ct] = sum[f][ct];
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            tile[(16 * f + 4 * g + r) * kDskCols + 16 * ct + c16] = gv * acc[f][ct][r];
     }
-    if (tid == 0) __hip_atomic_store(&p.counters[nt], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  // Output: wave 0 lays the tile out row-major in LDS (FP32, g applied), then
-  // every thread writes whole 16-byte pieces of the tile's rows -- one store
-  // per piece instead of one 2- or 4-byte store per element -- and only the
-  // pieces that reach past column N, or whose rows are not 16-byte aligned,
-  // go element by element.
-  float* tile = reinterpret_cast<float*>(xs);  // [BM][kDskCols]
-  __syncthreads();  // the exchange slots are free
-  if (wave == 0) {
-    const float gv = p.g[0];
-#pragma unroll
-    for (int f = 0; f < NF; ++f)
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          tile[(16 * f + 4 * g + r) * kDskCols + 16 * ct + c16] = gv * acc[f][ct][r];
-  }
+  // Output: the tile is row-major in LDS (FP32, g applied); every thread
+  // writes whole 16-byte pieces of the tile's rows -- one store per piece
+  // instead of one 2- or 4-byte store per element -- and only the pieces
+  // that reach past column N, or whose rows are not 16-byte aligned, go
+  // element by element.
+  const float* tile = reinterpret_cast<const float*>(xs);
   __syncthreads();
   const int esz = p.out_f32 ? 4 : 2;
   const int cpr = kDskCols * esz / 16;  // 16-byte pieces per tile row

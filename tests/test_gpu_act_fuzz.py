@@ -8,10 +8,11 @@ forced with the library's tuning overrides, with FP32 output (tolerance 1e-5
 of sum_k |x w|):
 
   kind 6  dot-product kernel (1-4 dense rows)
-  kind 7  MFMA decode kernel (5-16 dense rows, k % 128 == 0)
+  kind 7  MFMA decode kernel (5-8 dense rows, k % 128 == 0)
+  kind 8  split-K decode kernel (9-64 dense rows, k % 128 == 0)
   kind 4  K-phase kernel, 64-column tiles (dense <= 16 rows, NVFP4_GEMV=0)
-  kind 1  K-phase kernel, 4 waves x 128 columns (17-128 dense rows, or a
-          grouped launch with <= 32 rows per expert)
+  kind 1  K-phase kernel, 4 waves x 128 columns (65-128 dense rows, 17-64
+          with NVFP4_DSK=0, or a grouped launch with <= 32 rows per expert)
   kind 2  K-phase kernel, 8 waves x 256 columns (NVFP4_KPCFG=8 / 64-row tiles)
   kind 3  large-M kernel (NVFP4_LM=2, >= 256 rows)
   kind 0  register kernel (k % 64 != 0)
@@ -62,18 +63,26 @@ def act(m, k, family, seed):
 # (kind, m, n, k, overrides)
 DENSE_KINDS = [
     (6, 3, 200, 512, {}),
-    (7, 11, 200, 1024, {}),
+    (7, 7, 200, 1024, {}),
+    (8, 11, 200, 1024, {}),
+    (8, 40, 300, 1024, {}),
     (4, 9, 200, 1024, {"NVFP4_GEMV": 0}),
-    (1, 40, 300, 1024, {}),
-    (2, 40, 300, 1024, {"NVFP4_KPCFG": 8}),
+    (1, 40, 300, 1024, {"NVFP4_DSK": 0}),
+    (2, 40, 300, 1024, {"NVFP4_DSK": 0, "NVFP4_KPCFG": 8}),
     (3, 300, 300, 512, {"NVFP4_LM": 2}),
     (0, 20, 200, 208, {}),
 ]
+# kernel name prefix of each kind (the planner's choice is checked, so a
+# change of the planner cannot silently move a case off its kernel)
+KIND_NAME = {6: "nvfp4::gemv_kernel<", 7: "nvfp4::decode_mfma_kernel<",
+             8: "nvfp4::decode_sk_kernel<", 4: "nvfp4::gemm_kp_kernel<16, 5, 4, 64,",
+             1: "nvfp4::gemm_kp_kernel<32, 4, 4, 128,", 2: "nvfp4::gemm_kp_kernel<32, 5, 8, 256,",
+             3: "nvfp4::gemm_lm_kernel", 0: "nvfp4::gemm_reg_kernel<"}
 
 
 @pytest.mark.parametrize("family", FAMILIES)
 @pytest.mark.parametrize("kind,m,n,k,env", DENSE_KINDS,
-                         ids=["kind%d" % c[0] for c in DENSE_KINDS])
+                         ids=["kind%d_m%d" % (c[0], c[1]) for c in DENSE_KINDS])
 def test_dense(kind, m, n, k, env, family):
     nv = require_gpu()
     seed = kind * 100 + FAMILIES.index(family)
@@ -83,6 +92,8 @@ def test_dense(kind, m, n, k, env, family):
     y_ref, d = oracle.gemm(x, p, s, g[0])
     qw = nv.QuantizedWeight(dev(p), dev(s), dev(np.atleast_1d(g).astype(np.float32)))
     with EnvOverride(**env):
+        name = nv.load_library().nvfp4_kernel_name(m, 1, n, k, 0, 0).decode()
+        assert name.startswith(KIND_NAME[kind]), name
         y = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda")
         nv.gemm(dev(x), qw, out_dtype=torch.float32, out=y)
         torch.cuda.synchronize()

@@ -4,10 +4,12 @@ Decode products ("The FP4 Frontier", Finding 7: bandwidth-bound at small
 batch) with at most four token rows run on a kernel that keeps the block
 scale out of the inner loop: per 16-element block the exact E2M1 values are
 dotted with the activations in FP32, and the block's E4M3 scale multiplies
-that partial sum.  Five to sixteen rows (k % 128 == 0) run on one MFMA row
+that partial sum.  Five to eight rows (k % 128 == 0) run on one MFMA row
 tile per 16 columns with whole K per workgroup and a permuted K order inside
-each MFMA.  Same tolerances as every GEMM: FP32 output within 1e-5, BF16
-within 4e-3 of sum_k |x * w|."""
+each MFMA; from nine rows the split-K decode kernel takes over (its own
+tests are in test_gpu_decode_sk.py; the 13- and 16-row cases here run on it,
+with up to 128 splits of one K group at K = 16384).  Same tolerances as
+every GEMM: FP32 output within 1e-5, BF16 within 4e-3 of sum_k |x * w|."""
 import os
 
 import numpy as np

@@ -469,6 +469,49 @@ def moe_layer_extras(launches):
                                      "tokens": r.tokens, "topk": r.topk}}
 
 
+def mlp_extras(launches):
+    """The MoE MLP (gate_up with the SiLU(gate) * up epilogue, then the down
+    projection N = 6144, K = 2048) as one persistent launch, against the two
+    launches in a row (each planned on its own, K split where the planner
+    splits it).  ~64 tok/expert uses the Zipf down weight; ~16 tok/expert a
+    down weight drawn for it."""
+    import torch
+    import block_scaled_fp4_nibble_amd as nv
+
+    out = {}
+    down = next(L for L in launches if L["name"] == "down_zipf_64tpe")
+    for L in launches:
+        if not L["name"].startswith("up_"):
+            continue
+        if L["name"] == "up_zipf_64tpe":
+            qd = down["qw"]
+        else:
+            w = randn_bf16((L["experts"], down["n"], down["k"]), 0.02, 800)
+            qd = nv.quantize(w)
+            del w
+        rows = L["rows"]
+        h = torch.empty((rows, L["n"] // 2), dtype=torch.bfloat16, device="cuda")
+        y = torch.empty((rows, down["n"]), dtype=torch.bfloat16, device="cuda")
+
+        def fused():
+            nv.grouped_mlp(L["x"], L["off"], L["qw"], qd, out=y, h=h)
+
+        def two():
+            nv.grouped_gemm_swiglu(L["x"], L["off"], L["qw"], out=h)
+            nv.grouped_gemm(h, L["off"], qd, out=y)
+        ms_f = ms_t = float("inf")
+        for _ in range(2):
+            ms_f = min(ms_f, time_fn(fused, 20, 3))
+            ms_t = min(ms_t, time_fn(two, 20, 3))
+        flops = L["flops"] + 2 * rows * down["n"] * down["k"]
+        name = L["name"].replace("up_", "mlp_")
+        out[name] = {"us": ms_f * 1e3, "two_launches_us": ms_t * 1e3,
+                     "TFLOPS": flops / (ms_f * 1e-3) / 1e12,
+                     "kernel": nv.nvfp4_grouped_mlp_kernel_name(rows, L["experts"], down["n"],
+                                                                 down["k"])}
+    return out
+
+
 def w4a4_extras(launches):
     """The ~16 tok/expert up launch with NVFP4 activations: quantizing the
     activations, then the W4A4 launch (decode of the activations included),
@@ -672,6 +715,7 @@ def main():
         ex.update(combine_extras(launches))
         ex.update(w4a4_extras(launches))
         ex.update(moe_layer_extras(launches))
+        ex.update(mlp_extras(launches))
         ex.update(extras())
         # the same rates against what this box measured (context for the
         # spec peaks): the dominant kernel's algorithmic GB/s over a device

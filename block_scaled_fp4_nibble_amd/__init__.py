@@ -29,11 +29,13 @@ OUT_F32 = 1
 DSTATUS_NONFINITE = 1
 DSTATUS_BAD_OFFSETS = 2
 DSTATUS_BAD_INDEX = 4
+DSTATUS_WAIT_TIMEOUT = 8
 MAX_EXPERTS = 1024
 
 EXPORTED = [
     "nvfp4_quantize", "nvfp4_gemm", "nvfp4_grouped_gemm", "nvfp4_grouped_gemm_swiglu",
-    "nvfp4_grouped_gemm_gather", "nvfp4_moe_combine", "nvfp4_gemm_w4a4",
+    "nvfp4_grouped_gemm_gather", "nvfp4_grouped_mlp", "nvfp4_grouped_mlp_workspace_size",
+    "nvfp4_grouped_mlp_kernel_name", "nvfp4_moe_combine", "nvfp4_gemm_w4a4",
     "nvfp4_grouped_gemm_w4a4", "nvfp4_gemm_noalloc", "nvfp4_gemm_w4a4_workspace_size",
     "nvfp4_grouped_gemm_w4a4_workspace_size",
     "nvfp4_quantize_workspace_size",
@@ -77,6 +79,13 @@ def load_library(path: str = LIB_PATH):
         lib.nvfp4_grouped_gemm_gather.argtypes = [P, I64, P, I64, P, I64, I64, I64, P, P, P, P,
                                                   I32, I32, P, P, SZ, P]
         lib.nvfp4_grouped_gemm_gather.restype = I32
+        lib.nvfp4_grouped_mlp.argtypes = [P, I64, P, I64, I64, I64, P, P, P, P, P, P, P, P, I32,
+                                          P, P, SZ, P]
+        lib.nvfp4_grouped_mlp.restype = I32
+        lib.nvfp4_grouped_mlp_workspace_size.argtypes = [I64, I64, I64, I64]
+        lib.nvfp4_grouped_mlp_workspace_size.restype = SZ
+        lib.nvfp4_grouped_mlp_kernel_name.argtypes = [I64, I64, I64, I64]
+        lib.nvfp4_grouped_mlp_kernel_name.restype = ctypes.c_char_p
         lib.nvfp4_moe_combine.argtypes = [P, I32, I64, P, P, I64, I64, I64, P, I32, P, P]
         lib.nvfp4_moe_combine.restype = I32
         lib.nvfp4_gemm_w4a4.argtypes = [P, P, P, I64, I64, I64, P, P, P, P, I32, P, SZ, P]
@@ -184,6 +193,25 @@ def nvfp4_grouped_gemm_swiglu(x, rows, offsets, num_experts, n, k, packed, scale
         _ptr(x), rows, _ptr(offsets), num_experts, n, k, _ptr(packed), _ptr(scales),
         _ptr(global_scales), _ptr(h), out, _ptr(d_status), _ptr(workspace), ws_bytes,
         _stream(stream))
+
+
+def nvfp4_grouped_mlp(x, rows, offsets, num_experts, d_model, d_ff, up_packed, up_scales,
+                      up_global, down_packed, down_scales, down_global, h, y, out, d_status,
+                      workspace, ws_bytes, stream=None):
+    return load_library().nvfp4_grouped_mlp(
+        _ptr(x), rows, _ptr(offsets), num_experts, d_model, d_ff, _ptr(up_packed),
+        _ptr(up_scales), _ptr(up_global), _ptr(down_packed), _ptr(down_scales),
+        _ptr(down_global), _ptr(h), _ptr(y), out, _ptr(d_status), _ptr(workspace), ws_bytes,
+        _stream(stream))
+
+
+def nvfp4_grouped_mlp_workspace_size(rows, num_experts, d_model, d_ff) -> int:
+    return load_library().nvfp4_grouped_mlp_workspace_size(rows, num_experts, d_model, d_ff)
+
+
+def nvfp4_grouped_mlp_kernel_name(rows, num_experts, d_model, d_ff) -> str:
+    return load_library().nvfp4_grouped_mlp_kernel_name(rows, num_experts, d_model,
+                                                        d_ff).decode()
 
 
 def nvfp4_quantize_workspace_size(batch, n, k) -> int:
@@ -398,6 +426,38 @@ def grouped_gemm_swiglu(x: torch.Tensor, offsets: torch.Tensor, qw: QuantizedWei
                                      qw.scales, qw.global_scale, out, code, d_status, ws, nbytes,
                                      stream),
            "nvfp4_grouped_gemm_swiglu")
+    return out
+
+
+def grouped_mlp(x: torch.Tensor, offsets: torch.Tensor, qw_up: QuantizedWeight,
+                qw_down: QuantizedWeight, out_dtype=torch.bfloat16, out: torch.Tensor | None = None,
+                h: torch.Tensor | None = None, d_status: torch.Tensor | None = None,
+                stream=None) -> torch.Tensor:
+    """y [rows, d_model] = grouped_gemm(grouped_gemm_swiglu(x, qw_up), qw_down) in
+    one persistent launch (see nvfp4_grouped_mlp in include/nvfp4.h); the
+    intermediate goes to h [rows, d_ff] (allocated when not given).  Raises
+    NVFP4Error(UNSUPPORTED) for shapes the fused launch does not take."""
+    x = _bf16_2d_or_3d(x, "x")
+    rows, d_model = x.shape
+    if qw_up.packed.dim() != 3 or qw_up.k != d_model or qw_down.packed.dim() != 3:
+        raise ValueError("weights must be [E, n, k/2]; the up weight's k must match x")
+    E, n_up, _ = qw_up.packed.shape
+    d_ff = n_up // 2
+    if qw_down.packed.shape[0] != E or qw_down.n != d_model or qw_down.k != d_ff:
+        raise ValueError("down weight must be [E, d_model, d_ff/2]")
+    if offsets.dtype != torch.int32 or offsets.numel() != E + 1 or not offsets.is_cuda:
+        raise ValueError("offsets must be a device int32 tensor of E+1 entries")
+    code = OUT_F32 if out_dtype == torch.float32 else OUT_BF16
+    if out is None:
+        out = torch.empty((rows, d_model), dtype=out_dtype, device=x.device)
+    if h is None:
+        h = torch.empty((rows, d_ff), dtype=torch.bfloat16, device=x.device)
+    nbytes = nvfp4_grouped_mlp_workspace_size(rows, E, d_model, d_ff)
+    ws = _gemm_ws.get(nbytes, x.device, stream)
+    _check(nvfp4_grouped_mlp(x, rows, offsets.contiguous(), E, d_model, d_ff, qw_up.packed,
+                             qw_up.scales, qw_up.global_scale, qw_down.packed, qw_down.scales,
+                             qw_down.global_scale, h, out, code, d_status, ws, nbytes, stream),
+           "nvfp4_grouped_mlp")
     return out
 
 

@@ -233,6 +233,133 @@ nvfp4_status_t nvfp4_grouped_gemm_swiglu(const void* x_bf16, int64_t rows,
                   reinterpret_cast<hipStream_t>(stream), true, 1);
 }
 
+// ---- MoE MLP in one launch -----------------------------------------------------
+
+namespace {
+int env_or(const char* name, int dflt) {
+  const char* v = getenv(name);
+  return (v && *v) ? atoi(v) : dflt;
+}
+
+// The two products of a fused MoE MLP and the launch that runs both.
+struct MlpPlan {
+  nvfp4::GemmPlan up, down;
+  bool ok;
+  int grid;
+  size_t ws_bytes;  // the GEMM counter region (left untouched, so the buffer can be
+                    // shared with the GEMM calls), then per-row-tile counts of stored
+                    // gate_up column tiles
+};
+
+MlpPlan plan_mlp(int64_t rows, int64_t E, int64_t d_model, int64_t d_ff) {
+  MlpPlan m{};
+  const int cus = cu_count();
+  // no K split: the down tiles of the same launch keep the CUs busy
+  m.up = nvfp4::plan_gemm(rows, E, 2 * d_ff, d_model, true, cus, false);
+  m.down = nvfp4::plan_gemm(rows, E, d_model, d_ff, true, cus, false);
+  m.ok = nvfp4::plan_fusable(m.up, m.down) && nvfp4::plan_pairs_tiles(m.up);
+  if (!m.ok) return m;
+  // every workgroup must be resident at once (a down tile waits for gate_up
+  // tiles of other workgroups): at most one per resident slot of the fused
+  // kernel itself
+  const int slots = cus * nvfp4::fused_occupancy(m.up);
+  m.grid = std::max(1, std::min(slots, std::max(m.up.grid, m.down.grid)));
+  const int64_t row_tiles = (rows + m.up.bm - 1) / m.up.bm + std::min<int64_t>(E, rows);
+  m.ws_bytes = nvfp4::kCounterBytes + (((size_t)row_tiles * 4 + 255) & ~(size_t)255);
+  return m;
+}
+
+// 64-column multiples (whole 16-byte epilogue pieces, even 16-column tile
+// pairs for SiLU(gate) * up); widths the LDS-staged epilogue covers (the
+// first product's tiles are stored with device-scope stores only there)
+bool mlp_shape_ok(int64_t d_model, int64_t d_ff) {
+  return d_model % 64 == 0 && d_ff % 64 == 0 && 2 * d_ff <= nvfp4::kFixedStoreMaxN &&
+         d_model <= nvfp4::kFixedStoreMaxN;
+}
+}  // namespace
+
+size_t nvfp4_grouped_mlp_workspace_size(int64_t rows, int64_t num_experts, int64_t d_model,
+                                        int64_t d_ff) {
+  if (rows <= 0 || num_experts <= 0 || num_experts > NVFP4_MAX_EXPERTS || d_model <= 0 ||
+      d_ff <= 0 || !mlp_shape_ok(d_model, d_ff))
+    return 0;
+  const MlpPlan m = plan_mlp(rows, num_experts, d_model, d_ff);
+  return m.ok ? m.ws_bytes : 0;
+}
+
+nvfp4_status_t nvfp4_grouped_mlp(const void* x_bf16, int64_t rows,
+                                 const int32_t* expert_offsets, int64_t num_experts,
+                                 int64_t d_model, int64_t d_ff, const uint8_t* up_packed,
+                                 const uint8_t* up_scales, const float* up_global,
+                                 const uint8_t* down_packed, const uint8_t* down_scales,
+                                 const float* down_global, void* h, void* y, nvfp4_out_t out,
+                                 uint32_t* d_status, void* workspace, size_t ws_bytes,
+                                 void* stream) {
+  if (num_experts < 1 || d_model < 1 || d_ff < 1) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (num_experts > NVFP4_MAX_EXPERTS) return NVFP4_ERR_UNSUPPORTED;
+  nvfp4_status_t st = check_gemm_common(x_bf16, rows, 2 * d_ff, d_model, up_packed, up_scales,
+                                        up_global, h, NVFP4_OUT_BF16);
+  if (st != NVFP4_OK) return st;
+  st = check_gemm_common(h, rows, d_model, d_ff, down_packed, down_scales, down_global, y, out);
+  if (st != NVFP4_OK) return st;
+  if (!mlp_shape_ok(d_model, d_ff)) return NVFP4_ERR_UNSUPPORTED;
+  if (rows == 0) return NVFP4_OK;
+  if (expert_offsets == nullptr) return NVFP4_ERR_INVALID_ARGUMENT;
+  if ((reinterpret_cast<uintptr_t>(expert_offsets) & 3u) != 0) return NVFP4_ERR_MISALIGNED;
+  const MlpPlan m = plan_mlp(rows, num_experts, d_model, d_ff);
+  if (!m.ok) return NVFP4_ERR_UNSUPPORTED;
+  if (workspace == nullptr || ws_bytes < m.ws_bytes) return NVFP4_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return NVFP4_ERR_MISALIGNED;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  nvfp4::GemmParams p{};
+  p.x = static_cast<const uint16_t*>(x_bf16);
+  p.w = up_packed;
+  p.s = up_scales;
+  p.g = up_global;
+  p.offsets = expert_offsets;
+  p.y = h;
+  p.d_status = d_status;
+  p.rows = rows;
+  p.num_experts = (int32_t)num_experts;
+  p.n = (int32_t)(2 * d_ff);
+  p.k = (int32_t)d_model;
+  p.splits = 1;
+  p.k_split = m.up.k_split;
+  p.n_tiles = m.up.n_tiles;
+  p.total_units = -1;
+  p.out_f32 = 0;
+  p.act = 1;
+  p.w2 = down_packed;
+  p.s2 = down_scales;
+  p.g2 = down_global;
+  p.y2 = y;
+  p.n2 = (int32_t)d_model;
+  p.k2 = (int32_t)d_ff;
+  p.n_tiles2 = m.down.n_tiles;
+  p.out2_f32 = out == NVFP4_OUT_F32 ? 1 : 0;
+  uint32_t* counts =
+      reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + nvfp4::kCounterBytes);
+  p.rt_counters = counts;
+  // a wait polls about every microsecond: 2^17 polls are ~0.1 s, far beyond
+  // any wait of a resident grid.  NVFP4_MLP_SPIN and NVFP4_MLP_WAIT_EXTRA are
+  // test hooks (a tiny limit, and a target no count reaches, force the
+  // give-up path while every kernel still ends normally).
+  p.spin_limit = std::max(0, env_or("NVFP4_MLP_SPIN", 1 << 17));
+  p.wait_extra = std::max(0, env_or("NVFP4_MLP_WAIT_EXTRA", 0));
+  if (nvfp4::launch_fill_zero(counts, m.ws_bytes - nvfp4::kCounterBytes, s) != hipSuccess)
+    return NVFP4_ERR_HIP;
+  return hip_status(nvfp4::launch_gemm_fused(m.up, m.grid, p, s));
+}
+
+const char* nvfp4_grouped_mlp_kernel_name(int64_t rows, int64_t num_experts, int64_t d_model,
+                                          int64_t d_ff) {
+  if (rows <= 0 || num_experts <= 0 || d_model <= 0 || d_ff <= 0 ||
+      !mlp_shape_ok(d_model, d_ff))
+    return "";
+  const MlpPlan m = plan_mlp(rows, num_experts, d_model, d_ff);
+  return m.ok ? nvfp4::fused_kernel_name(m.up) : "";
+}
+
 // ---- GEMM without allocation ------------------------------------------------
 
 namespace {

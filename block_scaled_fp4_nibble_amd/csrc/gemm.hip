@@ -87,6 +87,9 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)(p);
 }
 
+// COH: a device-coherent load (sc1), for data another XCD wrote during the
+// same launch (which this XCD's L2 may hold stale).
+template <bool COH = false>
 __device__ __forceinline__ void lds_dma16(uint32_t lds, uint32_t voff, uint32_t soff,
                                           u32x4_t rsrc) {
   // the descriptor is uniform; say so, so that it stays in SGPRs
@@ -95,15 +98,26 @@ __device__ __forceinline__ void lds_dma16(uint32_t lds, uint32_t voff, uint32_t 
                  (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[2]),
                  (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[3])};
   uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc),
-        "s"(__builtin_amdgcn_readfirstlane(soff))
-      : "memory");
+  if constexpr (COH)
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "buffer_load_dwordx4 %2, %3, %4 offen sc1 lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc),
+          "s"(__builtin_amdgcn_readfirstlane(soff))
+        : "memory");
+  else
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc),
+          "s"(__builtin_amdgcn_readfirstlane(soff))
+        : "memory");
 }
 
 // Exclusive scan of one int per thread over a workgroup of THREADS threads.
@@ -158,10 +172,6 @@ struct Sched {
   int tmp[16];
   int flag;
 };
-
-// Widest output for which a row tile's bytes (at most 64 rows of FP32)
-// stay inside one 32-bit buffer range.
-constexpr int kFixedStoreMaxN = (1 << 23);
 
 // A uniform 32-bit load through the scalar cache (the data are inputs this
 // kernel never writes, so the load needs no ordering against its stores);
@@ -280,6 +290,7 @@ __device__ __forceinline__ float expert_g(const GemmParams& p, int e) {
 
 struct Unit {
   int e, ks, nt, tile, row0, row_end, k_beg, k_end;
+  int rt;  // row tile of the launch (experts' row tiles in schedule order)
 };
 
 // Work units are handed out in rounds of gridDim.x.  Within a round, unit
@@ -296,15 +307,23 @@ __device__ __forceinline__ int round_unit(int round, int w, int G) {
 
 // Units of expert e are ordered (column tile, split, row tile); the expert's
 // output tiles (for the split-K counters) are numbered units / splits.
-template <int BM>
-__device__ __forceinline__ Unit decode_unit(const Sched& sc, const GemmParams& p, int unit) {
+// P2: the second product of a fused launch, whose units (p.n_tiles column
+// tiles per row tile, no K split) follow the schedule built for the first
+// product's n1 column tiles: its unit prefix is the first's scaled by
+// p.n_tiles / n1.
+template <int BM, bool P2 = false>
+__device__ __forceinline__ Unit decode_unit(const Sched& sc, const GemmParams& p, int unit,
+                                            int n1 = 1) {
+  auto prefix = [&](int pos) {
+    return P2 ? sched_units[pos] / n1 * p.n_tiles : sched_units[pos];
+  };
   // schedule position: last one with units[pos] <= unit (empty experts have
   // equal bounds)
   const int E = p.num_experts;
   int lo = 0, hi = E;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (sched_units[mid] <= unit) lo = mid; else hi = mid;
+    if (prefix(mid) <= unit) lo = mid; else hi = mid;
   }
   const int pos = __builtin_amdgcn_readfirstlane(lo);
   Unit u;
@@ -321,12 +340,13 @@ __device__ __forceinline__ Unit decode_unit(const Sched& sc, const GemmParams& p
     seg1 = p.offsets ? (int)sload_u32(p.offsets, 4u * (uint32_t)(u.e + 1)) : (int)p.rows;
   }
   const int mtiles = (seg1 - seg0 + BM - 1) / BM;
-  const int local = unit - sched_units[pos];
+  const int local = unit - prefix(pos);
   const int mt = local % mtiles;
   const int rest = local / mtiles;
   u.ks = rest % p.splits;
   u.nt = rest / p.splits;
-  u.tile = sched_units[pos] / p.splits + u.nt * mtiles + mt;
+  u.tile = prefix(pos) / p.splits + u.nt * mtiles + mt;
+  u.rt = (P2 ? sched_units[pos] / n1 : sched_units[pos] / (p.n_tiles * p.splits)) + mt;
   u.row0 = seg0 + mt * BM;
   u.row_end = min(u.row0 + BM, seg1);
   u.k_beg = u.ks * p.k_split;
@@ -619,7 +639,9 @@ __device__ __forceinline__ KpU kp_unit(const GemmParams& p, const Unit& u) {
 // last stage can).
 // G: the unit's activation rows come through a row index (per-unit offsets
 // in u.xg instead of the unit-independent o.x).
-template <int BM, int NSLOT, int KW, int BN, bool TAIL = true, bool G = false>
+// COH: the activations come from the first product of a fused launch
+// (device-coherent loads).
+template <int BM, int NSLOT, int KW, int BN, bool TAIL = true, bool G = false, bool COH = false>
 __device__ __forceinline__ void kp_issue(uint32_t stage, u32x4_t rw, u32x4_t rx,
                                          const KpOffsets<BM, KW, BN>& o, int kc, int k_end,
                                          int wave, uint32_t xg0 = 0, uint32_t xg1 = 0) {
@@ -633,7 +655,7 @@ __device__ __forceinline__ void kp_issue(uint32_t stage, u32x4_t rw, u32x4_t rx,
     const int t = L::kXInstr >= KW ? wave * L::kXPerWave + tt : wave % L::kXInstr;
     const uint32_t xo = G ? (tt == 0 ? xg0 : xg1) : o.x[tt];
     const uint32_t voff = (tail && kc + o.xk[tt] >= k_end) ? kOffNone : xo;
-    lds_dma16(stage + L::kX + t * 1024, voff, (uint32_t)(kc * 2), rx);
+    lds_dma16<COH>(stage + L::kX + t * 1024, voff, (uint32_t)(kc * 2), rx);
   }
 }
 
@@ -744,6 +766,33 @@ __device__ __forceinline__ void kp_mma(f32x4_t (&acc)[BM / 16][NJ], const KpRegs
   }
 }
 
+// Dependency of a unit of a fused launch's second product: the count of
+// stored first-product column tiles of its row tile must reach `target`.
+// Each wave polls on its own (the count only grows, so the waves of a
+// workgroup agree).  A wave gives up after `limit` polls, sets
+// NVFP4_DSTATUS_WAIT_TIMEOUT and from then on does not wait at all
+// (`gave_up`), so a launch whose workgroups are not all resident still ends.
+struct KpWait {
+  const uint32_t* ctr;  // nullptr: nothing to wait for
+  uint32_t target;
+  int limit;
+  uint32_t* d_status;
+};
+
+__device__ __forceinline__ void kp_wait(const KpWait& w, bool& gave_up) {
+  if (w.ctr == nullptr || gave_up) return;
+  for (int i = 0;; ++i) {
+    const uint32_t v = __hip_atomic_load(w.ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (v >= w.target) return;
+    if (i >= w.limit) {
+      gave_up = true;
+      if (w.d_status != nullptr) atomicOr(w.d_status, NVFP4_DSTATUS_WAIT_TIMEOUT);
+      return;
+    }
+    __builtin_amdgcn_s_sleep(4);
+  }
+}
+
 // The K loop of one unit, for tiles whose rows fill NFE of the BM / 16 row
 // fragments (fragments past NFE are pure padding and are skipped).
 //
@@ -764,13 +813,15 @@ __device__ __forceinline__ void kp_mma(f32x4_t (&acc)[BM / 16][NJ], const KpRegs
 // when it is full), the iterations run in blocks of WS whose waits, window
 // issues and K checks are compile-time constants; the remaining iterations
 // take the general path.
-template <int BM, int NSLOT, int KW, int BN, int NFE, bool G>
+// COH: device-coherent activation loads (second product of a fused launch);
+// nxw: what the next unit waits for before its first prefetched load.
+template <int BM, int NSLOT, int KW, int BN, int NFE, bool G, bool COH = false>
 __device__ __forceinline__ void kp_kloop(f32x4_t (&acc)[BM / 16][2 * BN / KW / 16],
                                          uint8_t* ring, const KpU& cu, int sb0, int wb0, int pf,
                                          bool ex, const KpU& nx, int pn, uint32_t cxg0,
                                          uint32_t cxg1, uint32_t nxg0, uint32_t nxg1,
                                          const KpOffsets<BM, KW, BN>& off, int kp, int ch,
-                                         int wave, int lane) {
+                                         int wave, int lane, const KpWait& nxw, bool& gave_up) {
   using L = KpLayout<BM, NSLOT, KW, BN>;
   constexpr int NJ = L::kNJ;
   constexpr int D = NSLOT;  // stages in flight after an iteration's issue
@@ -791,9 +842,9 @@ __device__ __forceinline__ void kp_kloop(f32x4_t (&acc)[BM / 16][2 * BN / KW / 1
     if (st % WS == 0)
       kp_issue_scales<BM, NSLOT, KW, BN>(ring0 + wbuf(st / WS), cu.rs, off,
                                          cu.k_beg + st * kRingKC, wave);
-    kp_issue<BM, NSLOT, KW, BN, true, G>(ring0 + slot(st), cu.rw, cu.rx, off,
-                                         cu.k_beg + st * kRingKC, cu.k_end, wave, cxg0,
-                                         cxg1);
+    kp_issue<BM, NSLOT, KW, BN, true, G, COH>(ring0 + slot(st), cu.rw, cu.rx, off,
+                                              cu.k_beg + st * kRingKC, cu.k_end, wave, cxg0,
+                                              cxg1);
   };
   // loads this wave issued after those of stage lo, through stage hi, plus
   // the previous unit's epilogue stores when stage lo was issued before them
@@ -827,9 +878,9 @@ __device__ __forceinline__ void kp_kloop(f32x4_t (&acc)[BM / 16][2 * BN / KW / 1
     if constexpr ((T + D) % WS == 0)
       kp_issue_scales<BM, NSLOT, KW, BN>(ring0 + wbuf((c + D) / WS), cu.rs, off,
                                          cu.k_beg + (c + D) * kRingKC, wave);
-    kp_issue<BM, NSLOT, KW, BN, false, G>(ring0 + slot(c + D), cu.rw, cu.rx, off,
-                                          cu.k_beg + (c + D) * kRingKC, cu.k_end, wave, cxg0,
-                                          cxg1);
+    kp_issue<BM, NSLOT, KW, BN, false, G, COH>(ring0 + slot(c + D), cu.rw, cu.rx, off,
+                                               cu.k_beg + (c + D) * kRingKC, cu.k_end, wave,
+                                               cxg0, cxg1);
     kp_read<BM, NJ, NFE, BN, WS>(nxt, ring + slot(c + 1), ring + wbuf((c + 1) / WS), (T + 1) % WS,
                                  true, kp, ch, lane);
     kp_mma<BM, NJ, NFE>(acc, cur);
@@ -847,12 +898,13 @@ __device__ __forceinline__ void kp_kloop(f32x4_t (&acc)[BM / 16][2 * BN / KW / 1
         // first window (j = 0) goes first
         const int j = c + D - nch;
         if (j == 0) {
+          kp_wait(nxw, gave_up);  // the next unit's activations are stored
           kp_issue_scales<BM, NSLOT, KW, BN>(ring0 + wbuf(nwin), nx.rs, off, nx.k_beg, wave);
           nx_ops += SPW;
         }
-        kp_issue<BM, NSLOT, KW, BN, true, G>(ring0 + slot(c + D), nx.rw, nx.rx, off,
-                                             nx.k_beg + j * kRingKC, nx.k_end, wave, nxg0,
-                                             nxg1);
+        kp_issue<BM, NSLOT, KW, BN, true, G, COH>(ring0 + slot(c + D), nx.rw, nx.rx, off,
+                                                  nx.k_beg + j * kRingKC, nx.k_end, wave, nxg0,
+                                                  nxg1);
         nx_ops += LS;
       }
       kp_read<BM, NJ, NFE, BN, WS>(nxt, ring + slot(c + 1), ring + wbuf((c + 1) / WS),
@@ -893,7 +945,7 @@ __device__ __forceinline__ void kp_kloop(f32x4_t (&acc)[BM / 16][2 * BN / KW / 1
 // c ^ ((row >> 2) & MSK), which spreads the accumulator layout's writes (four
 // rows at one column per instruction) over the banks.  The last barrier lets
 // the next unit's loads reuse the slots.
-template <int BM, int NSLOT, int KW, int BN, int ESZ, bool GLU>
+template <int BM, int NSLOT, int KW, int BN, int ESZ, bool GLU, int CPOL = 0>
 __device__ __forceinline__ void kp_store_tile(const f32x4_t (&out)[BM / 16][BN / KW / 16],
                                               const GemmParams& p, const Unit& u, float gv,
                                               uint8_t* ring, int sl0, int wave, int lane) {
@@ -969,24 +1021,35 @@ __device__ __forceinline__ void kp_store_tile(const f32x4_t (&out)[BM / 16][BN /
       make_rsrc(static_cast<const char*>(p.y) + (int64_t)u.row0 * row_bytes,
                 (uint32_t)(rows * row_bytes));
 #pragma unroll
-  for (int i = 0; i < kSt; ++i) __builtin_amdgcn_raw_buffer_store_b128(v[i], ry, off[i], 0, 0);
+  for (int i = 0; i < kSt; ++i) __builtin_amdgcn_raw_buffer_store_b128(v[i], ry, off[i], 0, CPOL);
 }
 
-// GATHER: activation rows come through p.row_index (see kp_gather).
-template <int BM, int NSLOT, int KW, int BN, bool GATHER = false>
-__global__ __launch_bounds__(KW * 64) void gemm_kp_kernel(GemmParams p) {
+// The persistent loop of the K-phase kernel over `total` units of product p.
+// PH = 0: a plain launch.  PH = 1 / 2: the first / second product of a fused
+// gate_up -> down launch (FUSED kernels):
+//  - phase 1 stores its output tiles with device-scope (write-through) stores,
+//    waits until they have completed and then adds one to its row tile's
+//    count in p.rt_counters;
+//  - phase 2 reads the first product's output as its activations with
+//    device-scope loads, waits (bounded, kp_wait) until its row tile's count
+//    covers all n1 column tiles of the first product before the unit's first
+//    load (in the previous unit's tail when the unit is prefetched), and takes
+//    its global scales from p.g (the schedule's LDS copy holds the first
+//    product's).
+// The loop for a phase starts with an empty ring (no prefetch across phases).
+template <int BM, int NSLOT, int KW, int BN, bool GATHER, int PH>
+__device__ __forceinline__ void kp_units(const GemmParams& p, Sched& sc, uint8_t* ring,
+                                         int total, int n1, bool& gave_up) {
   using L = KpLayout<BM, NSLOT, KW, BN>;
-  static_assert(kp_fits_lds<BM, NSLOT, KW, BN>(), "LDS budget");
   constexpr int NF = BM / 16;
   constexpr int NJ = L::kNJ;
   constexpr int NH = NJ / 2;  // column tiles a wave keeps after the K-half exchange
   constexpr int CPS = L::kChunksPerStage;
-  __shared__ __attribute__((aligned(16))) uint8_t ring[L::kTotal];
-  __shared__ Sched sc;
+  constexpr bool P2 = PH == 2;
+  constexpr int kEpiCpol = PH == 1 ? kCpolDevice : 0;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int kp = wave & 1, ch = wave >> 1;
-  const int total = build_schedule<KW * 64, BM>(sc, p);
   const int G = gridDim.x;
   // the workgroup's units are round_unit(round, blockIdx.x, G) for rounds
   // while the unit id is below total (the grid may exceed the unit count of
@@ -1000,9 +1063,15 @@ __global__ __launch_bounds__(KW * 64) void gemm_kp_kernel(GemmParams p) {
   // first stages prefetched, behind that fixed store count
   const int nout_bytes = (p.act ? p.n / 2 : p.n) * (p.out_f32 ? 4 : 2);
   const bool can_pf = p.splits == 1 && p.n <= kFixedStoreMaxN && nout_bytes % 16 == 0;
+  auto wait_of = [&](const Unit& v) {
+    return P2 ? KpWait{p.rt_counters + v.rt, (uint32_t)(n1 + p.wait_extra), p.spin_limit,
+                       p.d_status}
+              : KpWait{nullptr, 0u, 0, nullptr};
+  };
+  auto decode = [&](int unit) { return decode_unit<BM, P2>(sc, p, unit, n1); };
 
   int round = 0;
-  Unit u = decode_unit<BM>(sc, p, first);
+  Unit u = decode(first);
   KpU cu = kp_unit<BN>(p, u);
   uint32_t cxg[2] = {0u, 0u}, nxg[2] = {0u, 0u};
   if constexpr (GATHER) kp_gather<BM, NSLOT, KW, BN>(cu, cxg, p, u, wave, lane);
@@ -1014,14 +1083,18 @@ __global__ __launch_bounds__(KW * 64) void gemm_kp_kernel(GemmParams p) {
     Unit un = u;
     KpU nx = cu;
     if (has_next) {
-      un = decode_unit<BM>(sc, p, nu);
+      un = decode(nu);
       nx = kp_unit<BN>(p, un);
       if constexpr (GATHER) kp_gather<BM, NSLOT, KW, BN>(nx, nxg, p, un, wave, lane);
     }
     const int pn = (has_next && can_pf && cu.nch >= NSLOT) ? min(L::kPrefetch, nx.nch) : 0;
-    const float gv = expert_g(p, u.e);
+    // a unit whose first stages were not prefetched waits here for its
+    // activations (a prefetched one waited before its first load)
+    if (P2 && pf == 0) kp_wait(wait_of(u), gave_up);
+    const float gv = P2 ? __uint_as_float(sload_u32(p.g, 4u * (uint32_t)u.e)) : expert_g(p, u.e);
     // 16-row fragments holding rows of this tile (the rest is padding)
     const int nf = min(NF, (u.row_end - u.row0 + 15) / 16);
+    const KpWait nxw = wait_of(un);
 
     f32x4_t acc[NF][NJ];
 #pragma unroll
@@ -1029,9 +1102,10 @@ __global__ __launch_bounds__(KW * 64) void gemm_kp_kernel(GemmParams p) {
 #pragma unroll
       for (int j = 0; j < NJ; ++j) acc[f][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-#define NVFP4_KLOOP(NFE)                                                                         \
-  kp_kloop<BM, NSLOT, KW, BN, NFE, GATHER>(acc, ring, cu, sb0, wb0, pf, ex, nx, pn, cxg[0], \
-                                           cxg[1], nxg[0], nxg[1], off, kp, ch, wave, lane)
+#define NVFP4_KLOOP(NFE)                                                                        \
+  kp_kloop<BM, NSLOT, KW, BN, NFE, GATHER, P2>(acc, ring, cu, sb0, wb0, pf, ex, nx, pn,         \
+                                               cxg[0], cxg[1], nxg[0], nxg[1], off, kp, ch,     \
+                                               wave, lane, nxw, gave_up)
     switch (nf) {
       case 1: NVFP4_KLOOP(1); break;
       case 2: NVFP4_KLOOP(NF >= 2 ? 2 : NF); break;
@@ -1079,14 +1153,29 @@ __global__ __launch_bounds__(KW * 64) void gemm_kp_kernel(GemmParams p) {
     if (can_pf) {
       const int sl0 = (sb0 + cu.nch + pn) % NSLOT;
       if (p.act) {
-        if (p.out_f32) kp_store_tile<BM, NSLOT, KW, BN, 4, true>(out, p, u, gv, ring, sl0, wave, lane);
-        else kp_store_tile<BM, NSLOT, KW, BN, 2, true>(out, p, u, gv, ring, sl0, wave, lane);
+        if (p.out_f32)
+          kp_store_tile<BM, NSLOT, KW, BN, 4, true, kEpiCpol>(out, p, u, gv, ring, sl0, wave, lane);
+        else
+          kp_store_tile<BM, NSLOT, KW, BN, 2, true, kEpiCpol>(out, p, u, gv, ring, sl0, wave, lane);
       } else {
-        if (p.out_f32) kp_store_tile<BM, NSLOT, KW, BN, 4, false>(out, p, u, gv, ring, sl0, wave, lane);
-        else kp_store_tile<BM, NSLOT, KW, BN, 2, false>(out, p, u, gv, ring, sl0, wave, lane);
+        if (p.out_f32)
+          kp_store_tile<BM, NSLOT, KW, BN, 4, false, kEpiCpol>(out, p, u, gv, ring, sl0, wave, lane);
+        else
+          kp_store_tile<BM, NSLOT, KW, BN, 2, false, kEpiCpol>(out, p, u, gv, ring, sl0, wave, lane);
       }
-    } else
+    } else {
       finish_tile<NF, NH, KW, BN>(out, p, u, gv, sc);
+    }
+    if constexpr (PH == 1) {
+      // the tile's stores have completed (write-through, device scope) before
+      // its row tile's count goes up; the wait also covers the next unit's
+      // prefetched loads, which were issued earlier
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (threadIdx.x == 0)
+        __hip_atomic_fetch_add(p.rt_counters + u.rt, 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
     if (!has_next) break;
     sb0 = (sb0 + cu.nch) % NSLOT;
     wb0 = (wb0 + (cu.nch + L::kWinStages - 1) / L::kWinStages) % L::kWinBufs;
@@ -1097,6 +1186,42 @@ __global__ __launch_bounds__(KW * 64) void gemm_kp_kernel(GemmParams p) {
     cxg[0] = nxg[0];
     cxg[1] = nxg[1];
     ++round;
+  }
+}
+
+// GATHER: activation rows come through p.row_index (see kp_gather).
+// FUSED: p is a fused gate_up -> down launch (its second product in p.w2 ...),
+// run as two phases of one persistent loop each.
+template <int BM, int NSLOT, int KW, int BN, bool GATHER = false, bool FUSED = false>
+__global__ __launch_bounds__(KW * 64) void gemm_kp_kernel(GemmParams p) {
+  static_assert(kp_fits_lds<BM, NSLOT, KW, BN>(), "LDS budget");
+  static_assert(!(GATHER && FUSED), "fused launches read pre-permuted rows");
+  __shared__ __attribute__((aligned(16))) uint8_t ring[KpLayout<BM, NSLOT, KW, BN>::kTotal];
+  __shared__ Sched sc;
+  const int total = build_schedule<KW * 64, BM>(sc, p);
+  bool gave_up = false;
+  if constexpr (!FUSED) {
+    kp_units<BM, NSLOT, KW, BN, GATHER, 0>(p, sc, ring, total, 1, gave_up);
+  } else {
+    if (total <= 0) return;
+    kp_units<BM, NSLOT, KW, BN, false, 1>(p, sc, ring, total, 1, gave_up);
+    // the second product: h = the first product's output as activations;
+    // its schedule is the first's (same experts and row tiles), scaled
+    __syncthreads();  // every wave is done with the ring
+    GemmParams q = p;
+    q.x = static_cast<const uint16_t*>(p.y);
+    q.w = p.w2;
+    q.s = p.s2;
+    q.g = p.g2;
+    q.y = p.y2;
+    q.n = p.n2;
+    q.k = p.k2;
+    q.k_split = p.k2;
+    q.n_tiles = p.n_tiles2;
+    q.out_f32 = p.out2_f32;
+    q.act = 0;
+    const int total2 = total / p.n_tiles * p.n_tiles2;
+    kp_units<BM, NSLOT, KW, BN, false, 2>(q, sc, ring, total2, p.n_tiles, gave_up);
   }
 }
 
@@ -1650,7 +1775,7 @@ static int occupancy_for(const GemmPlan& pl) {
 }
 
 GemmPlan plan_gemm(int64_t rows, int64_t num_experts, int64_t n, int64_t k, bool grouped,
-                   int cu_count) {
+                   int cu_count, bool allow_split) {
   GemmPlan pl{};
   pl.fast = (k % 64) == 0;
   // one to four dense rows: the dot-product kernel, 16 columns per workgroup,
@@ -1747,7 +1872,7 @@ GemmPlan plan_gemm(int64_t rows, int64_t num_experts, int64_t n, int64_t k, bool
   int splits = 1;
   const int64_t tiles_est = grouped ? std::min<int64_t>(num_experts, rows) * pl.n_tiles
                                     : max_tiles;
-  if (tiles_est < slots) {
+  if (allow_split && tiles_est < slots) {
     // as many splits as keep every unit in the first round (one more would
     // start a second round of mostly idle slots); each split keeps at least
     // kMinSplitStages K stages: below that the per-unit pipeline fill and the
@@ -1758,7 +1883,7 @@ GemmPlan plan_gemm(int64_t rows, int64_t num_experts, int64_t n, int64_t k, bool
     splits = (int)std::min<int64_t>(want, kmax);
   }
   const int force_s = env_int("NVFP4_SPLITK", 0);
-  if (force_s > 0) splits = force_s;
+  if (force_s > 0 && allow_split) splits = force_s;
   if (max_tiles > kMaxCounters) splits = 1;
   int64_t ksplit = (k + splits - 1) / splits;
   ksplit = (ksplit + align - 1) / align * align;
@@ -1808,8 +1933,8 @@ const char* plan_kernel_name(const GemmPlan& pl, bool gather) {
   }
   if (pl.kind == 3) return "nvfp4::gemm_lm_kernel";
 #define NVFP4_KP_NAME(BM, NS, KW, BN) \
-  return gather ? "nvfp4::gemm_kp_kernel<" #BM ", " #NS ", " #KW ", " #BN ", true>" \
-                : "nvfp4::gemm_kp_kernel<" #BM ", " #NS ", " #KW ", " #BN ", false>"
+  return gather ? "nvfp4::gemm_kp_kernel<" #BM ", " #NS ", " #KW ", " #BN ", true, false>" \
+                : "nvfp4::gemm_kp_kernel<" #BM ", " #NS ", " #KW ", " #BN ", false, false>"
   if (pl.kind == 1) {
     if (pl.bm == 16) NVFP4_KP_NAME(16, 5, 4, 128);
     NVFP4_KP_NAME(32, 4, 4, 128);
@@ -1857,6 +1982,52 @@ hipError_t launch_gemm(const GemmPlan& pl, const GemmParams& p, hipStream_t stre
     else hipLaunchKernelGGL(gemm_reg_kernel<64>, grid, block, pl.dyn_lds, stream, p);
   }
 #undef NVFP4_KP
+  return hipGetLastError();
+}
+
+bool plan_fusable(const GemmPlan& up, const GemmPlan& down) {
+  return (up.kind == 1 || up.kind == 2) && up.kind == down.kind && up.bm == down.bm &&
+         up.bn == down.bn && up.nslot == down.nslot && up.splits == 1 && down.splits == 1 &&
+         up.fast && down.fast;
+}
+
+// Resident workgroups per CU of the fused instantiation of a plan's kernel.
+int fused_occupancy(const GemmPlan& pl) {
+  const int dyn = pl.dyn_lds;
+  if (pl.kind == 1)
+    return pl.bm == 16 ? occupancy_of(gemm_kp_kernel<16, 5, 4, 128, false, true>, 256, dyn)
+                       : occupancy_of(gemm_kp_kernel<32, 4, 4, 128, false, true>, 256, dyn);
+  return pl.bm == 16 ? occupancy_of(gemm_kp_kernel<16, 5, 8, 256, false, true>, 512, dyn)
+         : pl.bm == 32 ? occupancy_of(gemm_kp_kernel<32, 5, 8, 256, false, true>, 512, dyn)
+                       : occupancy_of(gemm_kp_kernel<64, 4, 8, 256, false, true>, 512, dyn);
+}
+
+const char* fused_kernel_name(const GemmPlan& pl) {
+  if (pl.kind == 1)
+    return pl.bm == 16 ? "nvfp4::gemm_kp_kernel<16, 5, 4, 128, false, true>"
+                       : "nvfp4::gemm_kp_kernel<32, 4, 4, 128, false, true>";
+  return pl.bm == 16 ? "nvfp4::gemm_kp_kernel<16, 5, 8, 256, false, true>"
+         : pl.bm == 32 ? "nvfp4::gemm_kp_kernel<32, 5, 8, 256, false, true>"
+                       : "nvfp4::gemm_kp_kernel<64, 4, 8, 256, false, true>";
+}
+
+hipError_t launch_gemm_fused(const GemmPlan& pl, int grid, const GemmParams& p,
+                             hipStream_t stream) {
+  const dim3 g((unsigned)grid);
+#define NVFP4_KPF(BM, NS, KW, BN) \
+  hipLaunchKernelGGL((gemm_kp_kernel<BM, NS, KW, BN, false, true>), g, dim3(KW * 64), pl.dyn_lds, \
+                     stream, p)
+  if (pl.kind == 1) {
+    if (pl.bm == 16) NVFP4_KPF(16, 5, 4, 128);
+    else NVFP4_KPF(32, 4, 4, 128);
+  } else if (pl.kind == 2) {
+    if (pl.bm == 16) NVFP4_KPF(16, 5, 8, 256);
+    else if (pl.bm == 32) NVFP4_KPF(32, 5, 8, 256);
+    else NVFP4_KPF(64, 4, 8, 256);
+  } else {
+    return hipErrorInvalidValue;
+  }
+#undef NVFP4_KPF
   return hipGetLastError();
 }
 

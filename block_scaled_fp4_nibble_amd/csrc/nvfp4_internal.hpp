@@ -12,6 +12,10 @@ constexpr int kMaxExperts = NVFP4_MAX_EXPERTS;
 // Split-K tile counters live in the first kCounterBytes of a GEMM workspace.
 constexpr size_t kCounterBytes = 65536;
 constexpr int kMaxCounters = (int)(kCounterBytes / sizeof(uint32_t));
+// Widest output for which a row tile's bytes (at most 64 rows of FP32) stay
+// inside one 32-bit buffer range: the K-phase kernel's LDS-staged epilogue
+// (and so the fused launch's device-scope stores) needs it.
+constexpr int kFixedStoreMaxN = (1 << 23);
 
 // ---- quantize -----------------------------------------------------------
 int quantize_parts(int64_t n, int64_t k, int cu_count);
@@ -42,6 +46,16 @@ struct GemmParams {
   int32_t act;              // 1: y [rows][n / 2] = SiLU(gate) * up over 32-row gate/up groups
   const int32_t* row_index; // [rows]: routed row r reads x row row_index[r]; nullptr: row r
   int32_t x_rows;           // rows of x when row_index is given
+  // The second product of a fused gate_up -> down launch (kernels built with
+  // FUSED only): it reads the first product's output y as its activations.
+  const uint8_t* w2;        // [E][n2][k2/2]
+  const uint8_t* s2;        // [E][n2][k2/16]
+  const float* g2;          // [E]
+  void* y2;                 // [rows][n2]
+  int32_t n2, k2, n_tiles2, out2_f32;
+  uint32_t* rt_counters;    // per row tile of the first product: column tiles stored (zeroed)
+  int32_t spin_limit;       // polls before a wait gives up
+  int32_t wait_extra;       // added to every wait's target (0; a test sets 1 to force give-ups)
 };
 
 struct GemmPlan {
@@ -73,9 +87,17 @@ constexpr int64_t kGemvMaxXBytes = 65536;
 constexpr int kDskCols = 64;
 constexpr int kDskMaxGroups = 16;
 
+// allow_split false: never split K (the fused gate_up -> down launch).
 GemmPlan plan_gemm(int64_t rows, int64_t num_experts, int64_t n, int64_t k, bool grouped,
-                   int cu_count);
+                   int cu_count, bool allow_split = true);
 hipError_t launch_gemm(const GemmPlan& plan, const GemmParams& p, hipStream_t stream);
+// Fused gate_up -> down launch: both products planned with the same K-phase
+// kernel and no K split (false otherwise); `plan` is the first product's.
+bool plan_fusable(const GemmPlan& up, const GemmPlan& down);
+int fused_occupancy(const GemmPlan& plan);
+const char* fused_kernel_name(const GemmPlan& plan);
+hipError_t launch_gemm_fused(const GemmPlan& plan, int grid, const GemmParams& p,
+                             hipStream_t stream);
 const char* plan_kernel_name(const GemmPlan& plan, bool gather);
 hipError_t launch_gemv(const GemmPlan& plan, const GemmParams& p, hipStream_t stream);
 // True when every wave of the planned kernel ends with an even number of

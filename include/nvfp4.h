@@ -67,7 +67,11 @@
  *    NVFP4_DSTATUS_BAD_OFFSETS (grouped GEMM saw offsets that are not a
  *    non-decreasing prefix array from 0 to rows; nothing is written to y)
  *    and NVFP4_DSTATUS_BAD_INDEX (a gathered row's index lies outside
- *    [0, x_rows); that row computes as if its activations were zero).
+ *    [0, x_rows); that row computes as if its activations were zero) and
+ *    NVFP4_DSTATUS_WAIT_TIMEOUT (nvfp4_grouped_mlp: a workgroup's bounded
+ *    wait for another workgroup's results gave up -- possible only when the
+ *    launch's workgroups cannot all be resident at once; y is then
+ *    unspecified).
  *    Bits are only ever set (atomic OR), never cleared, by the library.
  *  - Workspace: a device buffer of at least the size the matching
  *    *_workspace_size() function returns (0: pass NULL).  For the two GEMM
@@ -102,6 +106,7 @@ typedef enum { NVFP4_OUT_BF16 = 0, NVFP4_OUT_F32 = 1 } nvfp4_out_t;
 #define NVFP4_DSTATUS_NONFINITE 1u
 #define NVFP4_DSTATUS_BAD_OFFSETS 2u
 #define NVFP4_DSTATUS_BAD_INDEX 4u
+#define NVFP4_DSTATUS_WAIT_TIMEOUT 8u
 
 /* Largest number of experts nvfp4_grouped_gemm accepts. */
 #define NVFP4_MAX_EXPERTS 1024
@@ -184,6 +189,45 @@ nvfp4_status_t nvfp4_grouped_gemm_gather(const void* x_bf16, int64_t x_rows,
                                          void* y, nvfp4_out_t out, int32_t act,
                                          uint32_t* d_status, void* workspace, size_t ws_bytes,
                                          void* stream);
+
+/* MoE MLP in one persistent launch ("The FP4 Frontier", Finding 5: fuse the
+ * gate_up GEMM, SiLU and the down GEMM into a single persistent kernel):
+ *   h = nvfp4_grouped_gemm_swiglu(x, up weights)      h [rows][d_ff]
+ *   y = nvfp4_grouped_gemm(h, down weights)           y [rows][d_model]
+ * over the same expert segments, with the results of those two calls (bit
+ * for bit: the same kernels and summation order).  x [rows][d_model] holds
+ * the routed rows sorted by expert; up_packed[e] [2 d_ff][d_model/2] (32-row
+ * gate/up groups, as for nvfp4_grouped_gemm_swiglu), up_scales, up_global[e];
+ * down_packed[e] [d_model][d_ff/2], down_scales, down_global[e].  h (caller-
+ * allocated, written: BF16) is the intermediate; y gets `out`.
+ * The launch's workgroups first compute every gate_up tile, then every down
+ * tile; a down tile waits (a bounded poll of a per-row-tile count in the
+ * workspace) until all gate_up tiles of its rows are stored.  The grid is
+ * sized so that all workgroups are resident; should one wait time out anyway
+ * (another kernel holding CUs), NVFP4_DSTATUS_WAIT_TIMEOUT is set, that
+ * workgroup stops waiting, and y is unspecified.
+ * Requirements: d_ff % 16 == 0, d_model % 64 == 0 and d_ff % 64 == 0, and a
+ * schedule in which both products take the same K-phase kernel with no K
+ * split; otherwise NVFP4_ERR_UNSUPPORTED and nothing is enqueued (the two
+ * calls above then compute the same result).  Workspace:
+ * nvfp4_grouped_mlp_workspace_size() bytes; the call zeroes its per-row-tile
+ * counts (after the first nvfp4_workspace_counter_bytes(), which it never
+ * touches) on `stream`, so the buffer may also serve the GEMM calls.
+ * Alignment, offsets and status as nvfp4_grouped_gemm. */
+nvfp4_status_t nvfp4_grouped_mlp(const void* x_bf16, int64_t rows,
+                                 const int32_t* expert_offsets, int64_t num_experts,
+                                 int64_t d_model, int64_t d_ff, const uint8_t* up_packed,
+                                 const uint8_t* up_scales, const float* up_global,
+                                 const uint8_t* down_packed, const uint8_t* down_scales,
+                                 const float* down_global, void* h, void* y, nvfp4_out_t out,
+                                 uint32_t* d_status, void* workspace, size_t ws_bytes,
+                                 void* stream);
+size_t nvfp4_grouped_mlp_workspace_size(int64_t rows, int64_t num_experts, int64_t d_model,
+                                        int64_t d_ff);
+/* Name of the kernel instantiation nvfp4_grouped_mlp launches for this shape
+ * ("" when the shape is not supported). */
+const char* nvfp4_grouped_mlp_kernel_name(int64_t rows, int64_t num_experts, int64_t d_model,
+                                          int64_t d_ff);
 
 /* MoE combine, the scatter half of the routing-aware MoE layer ("The FP4
  * Frontier", Finding 5): out[t][c] = sum_j weights[t][j] * y[token_rows[t][j]][c]

@@ -178,6 +178,43 @@ def test_w4a4_host_validation(lib):
     assert gcall(rows=0, off=None) == 0
 
 
+def test_grouped_mlp_host_validation(lib):
+    def call(E=4, offsets=A, rows=8, d_model=128, d_ff=64, h=A, y=A, out=nv.OUT_BF16):
+        return nv.nvfp4_grouped_mlp(A, rows, offsets, E, d_model, d_ff, A, A, A, A, A, A, h, y,
+                                    out, None, None, 0, S)
+    assert call(E=0) == 1
+    assert call(E=nv.MAX_EXPERTS + 1) == 3
+    assert call(d_model=40) == 1             # not a multiple of 16
+    assert call(d_model=96) == 3             # 64-column tiles only: unsupported, never silent
+    assert call(d_ff=32) == 3
+    assert call(out=7) == 1
+    assert call(h=None) == 1
+    assert call(y=MIS) == 2
+    assert call(offsets=None) == 1
+    assert call(offsets=FakePtr(0x10002)) == 2
+    assert call(rows=0, offsets=None) == 0
+    assert nv.nvfp4_grouped_mlp_workspace_size(8, 4, 96, 64) == 0
+    assert nv.nvfp4_grouped_mlp_kernel_name(8, 4, 96, 64) == ""
+
+
+@pytest.mark.parametrize("rows,E,d_model,d_ff,bm", [
+    (512 * 8, 64, 6144, 2048, 64),   # ~64 rows per expert
+    (128 * 8, 64, 6144, 2048, 32),   # ~16 rows per expert
+    (333, 8, 512, 256, 64),
+    (200, 4, 256, 128, 64),
+    (8, 1, 128, 64, 16),
+])
+def test_grouped_mlp_plan(lib, rows, E, d_model, d_ff, bm):
+    """The fused launch takes the grouped GEMM's K-phase kernel for the row
+    tile its average rows per expert select, and its workspace is the GEMM
+    counter region plus one 32-bit count per possible row tile."""
+    name = nv.nvfp4_grouped_mlp_kernel_name(rows, E, d_model, d_ff)
+    assert name.startswith("nvfp4::gemm_kp_kernel<%d," % bm) and name.endswith("false, true>"), name
+    ws = nv.nvfp4_grouped_mlp_workspace_size(rows, E, d_model, d_ff)
+    row_tiles = -(-rows // bm) + min(E, rows)
+    assert ws == nv.nvfp4_workspace_counter_bytes() + -(-(4 * row_tiles) // 256) * 256
+
+
 def test_quantize_host_validation(lib):
     def call(batch=1, n=4, k=32, w=A, ws=None):
         return nv.nvfp4_quantize(w, batch, n, k, A, A, A, None, ws, 0, S)

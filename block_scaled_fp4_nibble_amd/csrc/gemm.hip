@@ -1227,44 +1227,56 @@ __global__ __launch_bounds__(KW * 64) void gemm_kp_kernel(GemmParams p) {
 
 // ---- large-M kernel (k % 64 == 0, many rows) -----------------------------------
 //
-// For a dense product with at least a few hundred rows the weight tile is
-// worth dequantizing once into LDS and sharing across a large row tile: a
-// 256 x 256 output tile per workgroup of 8 waves, each wave a 128 x 64 block
-// of 4 x 2 v_mfma_f32_32x32x16_bf16 tiles (FP32 accumulators).  Two waves
-// share each SIMD, so one wave's dequantization, LDS and load-issue work can
-// run while the other's MFMAs occupy the matrix pipeline.  K advances in
-// 64-wide steps.  LDS holds two slots each of the activation tile (256 rows
-// x 128 B) and the packed weight tile (256 rows x 32 B), two BF16 weight
-// tiles (256 rows x 128 B) and two scale windows of 4 steps (256 rows x
-// 16 B).  One barrier per step; after it each wave runs step s's 32 MFMAs
-// from activation slot s % 2 and BF16 tile s % 2, and between them issues
-// the loads of later steps, dequantizes its 32 weight rows of step s + 1 and
-// writes them into BF16 tile (s + 1) % 2.
+// For a dense product with at least a few hundred rows a 256 x 256 output
+// tile per workgroup of 8 waves amortizes the activation and weight traffic:
+// wave w = (wm, wn) computes rows [128 wm, 128 wm + 128) x columns
+// [64 wn, 64 wn + 64) of the tile as 4 x 2 v_mfma_f32_32x32x16_bf16 tiles
+// (FP32 accumulators).  Two waves share each SIMD, so one wave's
+// dequantization and load issue run while the other's MFMAs occupy the
+// matrix pipeline.  K advances in 64-wide steps.  LDS holds a 4-slot ring of
+// activation tiles (256 rows x 128 B), a 3-slot ring of packed weight tiles
+// (256 rows x 32 B, only the 4.5-bit data) and two windows of block scales
+// covering 4 steps each (256 rows x 16 B, one 16-byte load per row: a load
+// per row and step of 4 bytes cost 6 % of the launch).  During step s
+// (between its MFMA sub-steps, so the load path works while the matrix pipe
+// does) the weights of step s + 2 (with the scale window that starts there)
+// and the activations of step s + 3 are issued, and the barrier at the top
+// of step s waits only for step s's own loads.  Every workgroup of an XCD reads the same activation rows at about
+// the same time, so each activation step is in effect a miss to HBM for all
+// of them; three steps of lead hide that latency where two did not (8192^3:
+// 941 -> 848 us in a timing copy).  Weight lines (128 B = four steps of a
+// row) miss once in four steps, and two steps of lead cover them.  Each wave
+// dequantizes its own 64 columns of the step from the packed bytes in
+// registers; the two waves sharing a column range both do, which costs VALU
+// time the MFMAs of the other wave hide, and keeps BF16 weights out of LDS.
 //
-// LDS rows of the activation and BF16 weight tiles keep their 16-byte
-// chunk c in slot c ^ ((r >> 1) & 7), so the 32-row fragment reads and the
-// dequantizer's row writes spread over all banks.
+// K slots: in sub-step ks (16 K) of a step, lane l (row / column l % 32,
+// half h = l / 32) supplies K = 32 h + 8 ks .. + 7 of the step, for both
+// operands (the MFMA sums over its 16 K slots in any assignment as long as A
+// and B agree).  So a lane's weight bytes for the whole step are 16
+// contiguous bytes of its column, and each dword of them is one sub-step.
+// LDS rows of the activation tile keep their 16-byte chunk c in slot
+// c ^ ((r >> 1) & 7), so the 32-row fragment reads spread over all banks.
 constexpr int kLmBM = 256, kLmBN = 256, kLmBK = 64;
 
 struct LmLayout {
   static constexpr int kWaves = 8;
+  static constexpr int kXSlots = 4;                          // activation steps ahead: 3
+  static constexpr int kWSlots = 3;                          // weight steps ahead: 2
   static constexpr int kXStage = kLmBM * kLmBK * 2;          // 32 KB
   static constexpr int kWpStage = kLmBN * kLmBK / 2;         // 8 KB
-  static constexpr int kWbfBytes = kLmBN * kLmBK * 2;        // 32 KB
-  // two activation slots, two packed-weight slots, two BF16 weight tiles,
-  // two scale windows
-  static constexpr int kX = 0;
-  static constexpr int kWp = 2 * kXStage;
-  static constexpr int kWbf = kWp + 2 * kWpStage;
-  static constexpr int kWin = kWbf + 2 * kWbfBytes;
-  static constexpr int kWinBytes = kLmBN * 16;
-  static constexpr int kTotal = kWin + 2 * kWinBytes;
+  static constexpr int kWinSteps = 4;                        // steps per scale window
+  static constexpr int kWinBytes = kLmBN * kWinSteps * 4;    // 4 KB: 16 B per weight row
+  static constexpr int kW = kXSlots * kXStage;               // first packed weight slot
+  static constexpr int kWin = kW + kWSlots * kWpStage;       // first scale window
+  static constexpr int kTotal = kWin + 2 * kWinBytes;        // 160 KB
   static constexpr int kXLoads = kXStage / 1024 / kWaves;    // per wave per step: 4
   static constexpr int kWpLoads = kWpStage / 1024 / kWaves;  // per wave per step: 1
   static constexpr int kWinLoads = kWinBytes / 1024;         // waves 0..3, one each
-  static constexpr int kLoadsPerStage = kXLoads + kWpLoads;
+  static constexpr int kEpiBytes = 32 * 32 * 4;              // per wave: one FP32 32 x 32 tile
   static_assert(kTotal <= 160 * 1024, "LDS budget");
-  static_assert(kXLoads >= 1 && kWpLoads >= 1 && kWinLoads <= kWaves, "load split");
+  static_assert(kXLoads == 4 && kWpLoads == 1 && kWinLoads <= kWaves, "load split");
+  static_assert(kWaves * kEpiBytes <= kW, "epilogue scratch");
 };
 
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
@@ -1273,7 +1285,7 @@ __device__ __forceinline__ int lm_swz(int r, int c) { return r * 128 + 16 * (c ^
 
 struct LmOffsets {
   uint32_t x[LmLayout::kXLoads];
-  uint32_t wp[LmLayout::kWpLoads];
+  uint32_t wp;
   uint32_t s;
 };
 
@@ -1287,121 +1299,50 @@ __device__ __forceinline__ LmOffsets lm_offsets(int K, int wave, int lane) {
     const int g = (lane & 7) ^ ((r >> 1) & 7);
     o.x[tt] = (uint32_t)r * (uint32_t)(K * 2) + (uint32_t)(16 * g);
   }
-  // packed weights: load t covers rows 32t..32t+31 (32 B each, unswizzled)
-#pragma unroll
-  for (int tt = 0; tt < LmLayout::kWpLoads; ++tt) {
-    const int r = (wave * LmLayout::kWpLoads + tt) * 32 + (lane >> 1);
-    o.wp[tt] = (uint32_t)r * (uint32_t)(K / 2) + (uint32_t)(16 * (lane & 1));
-  }
-  // scale window: wave w < 4 loads rows 64w..64w+63, 16 B (256 K) each
+  // packed weights: wave w loads rows 32w..32w+31 (32 B each, unswizzled)
+  o.wp = (uint32_t)(wave * 32 + (lane >> 1)) * (uint32_t)(K / 2) + (uint32_t)(16 * (lane & 1));
+  // scale window: wave w < 4 loads rows 64w..64w+63, 16 B (4 steps) each
   o.s = (uint32_t)((wave & 3) * 64 + lane) * (uint32_t)(K / 16);
   return o;
 }
 
-// The packed weights of a step (and, with the first step it covers, a scale
-// window) into weight slot step % 2.
+// The packed weights of a step into its weight slot, preceded (every
+// kWinSteps-th step, waves 0..3) by the scale window that starts there.
 __device__ __forceinline__ void lm_issue_w(uint32_t ring0, int step, u32x4_t rw, u32x4_t rs,
                                            const LmOffsets& o, int wave) {
-  if (step % 4 == 0 && wave < LmLayout::kWinLoads)
-    lds_dma16(ring0 + LmLayout::kWin + ((step / 4) & 1) * LmLayout::kWinBytes + wave * 1024, o.s,
+  using L = LmLayout;
+  if (step % L::kWinSteps == 0 && wave < L::kWinLoads)
+    lds_dma16(ring0 + L::kWin + ((step / L::kWinSteps) & 1) * L::kWinBytes + wave * 1024, o.s,
               (uint32_t)(step * kLmBK / 16), rs);
-  const uint32_t st = ring0 + LmLayout::kWp + (step & 1) * LmLayout::kWpStage;
-#pragma unroll
-  for (int tt = 0; tt < LmLayout::kWpLoads; ++tt)
-    lds_dma16(st + (wave * LmLayout::kWpLoads + tt) * 1024, o.wp[tt], (uint32_t)(step * kLmBK / 2),
-              rw);
+  lds_dma16(ring0 + L::kW + (uint32_t)((step % L::kWSlots) * L::kWpStage) + wave * 1024, o.wp,
+            (uint32_t)(step * kLmBK / 2), rw);
 }
 
-// The activations of a step into activation slot step % 2.
-__device__ __forceinline__ void lm_issue_x(uint32_t ring0, int step, u32x4_t rx,
+// Load tt (of four) of a step's activations into its slot.
+__device__ __forceinline__ void lm_issue_x(uint32_t ring0, int step, int tt, u32x4_t rx,
                                            const LmOffsets& o, int wave) {
-  const uint32_t st = ring0 + LmLayout::kX + (step & 1) * LmLayout::kXStage;
-#pragma unroll
-  for (int tt = 0; tt < LmLayout::kXLoads; ++tt)
-    lds_dma16(st + (wave * LmLayout::kXLoads + tt) * 1024, o.x[tt], (uint32_t)(step * kLmBK * 2),
-              rx);
+  const uint32_t st = ring0 + (uint32_t)((step % LmLayout::kXSlots) * LmLayout::kXStage);
+  lds_dma16(st + (wave * LmLayout::kXLoads + tt) * 1024, o.x[tt], (uint32_t)(step * kLmBK * 2), rx);
 }
 
-// One lane's share of a weight step: half h = lane % 2 (32 K) of row
-// 32 wave + lane / 2, as 4 dwords of nibbles and the row's 4 block scales of
-// the step shifted so that the lane's two are in bytes 0 and 1 (decoded
-// where they are used, so the LDS read is not waited for early).
-struct LmWp {
-  uint32_t d[4];
-  uint32_t sc;
-};
-
-__device__ __forceinline__ void lm_read_wp(LmWp& w, const uint8_t* ring, int step, int wave, int lane) {
-  const int r = wave * 32 + (lane >> 1), h = lane & 1;
-  const uint8_t* wp = ring + LmLayout::kWp + (step & 1) * LmLayout::kWpStage + r * 32;
-  const u32x4_t d = *reinterpret_cast<const u32x4_t*>(wp + 16 * h);
-  const uint32_t sc = *reinterpret_cast<const uint32_t*>(
-      ring + LmLayout::kWin + ((step / 4) & 1) * LmLayout::kWinBytes + r * 16 + 4 * (step % 4));
-#pragma unroll
-  for (int c = 0; c < 4; ++c) w.d[c] = d[c];
-  w.sc = sc >> (16 * h);
-}
-
-// Write chunk c (8 BF16) of a lane's dequantized weights into BF16 weight
-// tile `buf`.
-__device__ __forceinline__ void lm_write_wbf1(uint8_t* ring, int buf, const bf16x8_t& v, int c,
-                                              int wave, int lane) {
-  const int r = wave * 32 + (lane >> 1), h = lane & 1;
-  uint8_t* wb = ring + LmLayout::kWbf + buf * LmLayout::kWbfBytes;
-  *reinterpret_cast<bf16x8_t*>(wb + lm_swz(r, 4 * h + c)) = v;
-}
-
-// Write a lane's 4 dequantized chunks into BF16 weight tile `buf`.
-__device__ __forceinline__ void lm_write_wbf(uint8_t* ring, int buf, const bf16x8_t (&v)[4],
-                                             int wave, int lane) {
-#pragma unroll
-  for (int c = 0; c < 4; ++c) lm_write_wbf1(ring, buf, v[c], c, wave, lane);
-}
-
-// 32 MFMAs of one step for the wave's 128 x 64 block: 4 K sub-steps of 16,
-// each reading 4 A and 2 B fragments (lane l: row / column l % 32, K 8 (l /
-// 32) .. +7 of the sub-step).  The lane's share of the next step's weights
-// is dequantized between the MFMAs (one chunk per sub-step), where its VALU
-// work overlaps the matrix pipeline.
-__device__ __forceinline__ void lm_frags(bf16x8_t (&a)[4], bf16x8_t (&b)[2], const uint8_t* xs,
-                                         const uint8_t* wb, int ks, int wm, int wn, int lane) {
+// Activation fragments of sub-step ks: 4 row tiles of the wave's 128 rows.
+__device__ __forceinline__ void lm_read_a(bf16x8_t (&a)[4], const uint8_t* st, int ks, int wm,
+                                          int lane) {
   const int r32 = lane & 31, h = lane >> 5;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    a[i] = *reinterpret_cast<const bf16x8_t*>(xs + lm_swz(wm * 128 + i * 32 + r32, 2 * ks + h));
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-    b[j] = *reinterpret_cast<const bf16x8_t*>(wb + lm_swz(wn * 64 + j * 32 + r32, 2 * ks + h));
-}
-
-template <class Hook>
-__device__ __forceinline__ void lm_mma(f32x16_t (&acc)[4][2], const uint8_t* xs, const uint8_t* wb,
-                                       int wm, int wn, int lane, bool dq, const LmWp& w,
-                                       bf16x8_t (&v)[4], Hook hook) {
-  // fragments of sub-step ks + 1 are read while sub-step ks is multiplied
-  bf16x8_t a[2][4], b[2][2];
-  lm_frags(a[0], b[0], xs, wb, 0, wm, wn, lane);
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    if (ks + 1 < 4) lm_frags(a[(ks + 1) & 1], b[(ks + 1) & 1], xs, wb, ks + 1, wm, wn, lane);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks & 1][i], b[ks & 1][j], acc[i][j],
-                                                            0, 0, 0);
-    if (dq) v[ks] = dequant8(w.d[ks], (ks >> 1) ? decode_e4m3<1>(w.sc) : decode_e4m3<0>(w.sc));
-    hook(ks);
-  }
+    a[i] = *reinterpret_cast<const bf16x8_t*>(st + lm_swz(wm * 128 + i * 32 + r32, 4 * h + ks));
 }
 
 // Dense only (offsets == nullptr, one expert): tile t of the grid is
 // (row tile t / n_tiles, column tile t % n_tiles) after an XCD-aware remap.
 __global__ __launch_bounds__(LmLayout::kWaves * 64) void gemm_lm_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t ring[LmLayout::kTotal];
+  using L = LmLayout;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[L::kTotal];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 2, wn = wave & 3;  // 128-row half, 64-column quarter
+  const int r32 = lane & 31, h = lane >> 5;
   const int N = p.n, K = p.k;
   const int m_tiles = (int)((p.rows + kLmBM - 1) / kLmBM);
   const int total = m_tiles * p.n_tiles;
@@ -1409,6 +1350,19 @@ __global__ __launch_bounds__(LmLayout::kWaves * 64) void gemm_lm_kernel(GemmPara
   const LmOffsets off = lm_offsets(K, wave, lane);
   const int nsteps = K / kLmBK;
   const float gv = p.g[0];
+  const int ob = p.out_f32 ? 4 : 2;
+  // the epilogue writes whole 16-column pieces of rows when every piece is
+  // 16-byte aligned, none straddles the last column and a tile's rows stay
+  // inside one 32-bit buffer range
+  const bool vec_out = N % 16 == 0 && (int64_t)kLmBM * N * ob < ((int64_t)1 << 31);
+  // the lane's weight bytes within a weight slot and its scales within a
+  // window, per column tile j
+  uint32_t wp_at[2], s_at[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    wp_at[j] = (uint32_t)((wn * 64 + j * 32 + r32) * 32 + 16 * h);
+    s_at[j] = (uint32_t)((wn * 64 + j * 32 + r32) * 16);
+  }
 
   for (int round = 0; round * (int)gridDim.x < total; ++round) {
     const int t = round_unit(round, blockIdx.x, gridDim.x);
@@ -1430,69 +1384,137 @@ __global__ __launch_bounds__(LmLayout::kWaves * 64) void gemm_lm_kernel(GemmPara
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-    // Pipeline per iteration s: wait for everything issued (the activations
-    // of step s and the packed weights of step s + 1, issued last, in
-    // iteration s - 1), barrier, issue the packed weights of step s + 2 and
-    // the activations of step s + 1 into the slots step s - 1 and step s - 2
-    // used, then run step s's MFMAs from BF16 tile s % 2 with step s + 1's
-    // weights dequantized between them and written into BF16 tile
-    // (s + 1) % 2, which step s - 1's MFMAs were done with at the barrier.
-    LmWp wq;
-    bf16x8_t v[4];
-    lm_issue_w(ring0, 0, rw, rs, off, wave);
-    lm_issue_x(ring0, 0, rx, off, wave);
-    if (nsteps > 1) lm_issue_w(ring0, 1, rw, rs, off, wave);
-    wait_vmcnt_c<0>();
-    __syncthreads();
-    lm_read_wp(wq, ring, 0, wave, lane);
+    // The issue order is that of steady state from virtual step -3 on: in
+    // step v, the weights of step v + 2, then the activations of step v + 3.
+    // So after the weights of step s come the activations of step s + 1 and
+    // the weights of step s + 1 (at least 5 loads per wave, if step s + 1
+    // exists) and the activations of step s + 2 (4, if it exists); the
+    // activations of step s went out before the weights of step s.  (A scale
+    // window among the weights of step s + 1 makes the wait below cover one
+    // load more than it must.)
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-      v[c] = dequant8(wq.d[c], (c >> 1) ? decode_e4m3<1>(wq.sc) : decode_e4m3<0>(wq.sc));
-    lm_write_wbf(ring, 0, v, wave, lane);
-
-    for (int s = 0; s < nsteps; ++s) {
-      const bool more = s + 1 < nsteps;
-      wait_vmcnt_c<0>();
-      __syncthreads();
-      if (more) lm_read_wp(wq, ring, s + 1, wave, lane);
-      // the next steps' loads go out between the MFMA sub-steps, so the
-      // load path works while the matrix pipe does (issued all at once after
-      // the barrier they held every wave for hundreds of cycles); so does
-      // each chunk of the next step's BF16 weight tile as soon as it is
-      // dequantized (that buffer's readers, step s - 1, all passed the
-      // barrier above)
-      auto issue = [&](int ks) {
-        if (ks == 0 && s + 2 < nsteps) lm_issue_w(ring0, s + 2, rw, rs, off, wave);
-        if (ks == 1 && more) lm_issue_x(ring0, s + 1, rx, off, wave);
-        if (more) lm_write_wbf1(ring, (s + 1) & 1, v[ks], ks, wave, lane);
-      };
-      lm_mma(acc, ring + LmLayout::kX + (s & 1) * LmLayout::kXStage,
-             ring + LmLayout::kWbf + (s & 1) * LmLayout::kWbfBytes, wm, wn, lane, more, wq, v,
-             issue);
+    for (int tt = 0; tt < L::kXLoads; ++tt) lm_issue_x(ring0, 0, tt, rx, off, wave);
+    for (int v = 0; v < 2; ++v) {
+      if (v < nsteps) lm_issue_w(ring0, v, rw, rs, off, wave);
+      if (v + 1 < nsteps) {
+#pragma unroll
+        for (int tt = 0; tt < L::kXLoads; ++tt) lm_issue_x(ring0, v + 1, tt, rx, off, wave);
+      }
     }
-    __syncthreads();  // all fragment reads done before the next tile's loads
-
-    // epilogue: lane l of tile (i, j) holds column l % 32 and rows
-    // 8 (e / 4) + 4 (l / 32) + e % 4 of the 32 x 32 block
-    const int r32 = lane & 31, h = lane >> 5;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int s = 0; s < nsteps; ++s) {
+      // this wave's loads of step s are done; the barrier makes every
+      // wave's done, and every wave is past step s - 1, whose slots the
+      // loads issued in this step take
+      if (s + 2 < nsteps) wait_vmcnt_c<L::kXLoads + L::kWpLoads + L::kXLoads>();
+      else if (s + 1 < nsteps) wait_vmcnt_c<L::kXLoads + L::kWpLoads>();
+      else wait_vmcnt_c<0>();
+      __syncthreads();
+      const uint8_t* st = ring + (s % L::kXSlots) * L::kXStage;
+      const uint8_t* wst = ring + L::kW + (s % L::kWSlots) * L::kWpStage;
+      const uint8_t* win = ring + L::kWin + ((s / L::kWinSteps) & 1) * L::kWinBytes +
+                           4 * (s % L::kWinSteps);
+      const bool prew = s + 2 < nsteps, prex = s + 3 < nsteps;
+      u32x4_t wd[2];
+      uint32_t sc[2];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const int col = n0 + wn * 64 + j * 32 + r32;
+        wd[j] = *reinterpret_cast<const u32x4_t*>(wst + wp_at[j]);
+        sc[j] = *reinterpret_cast<const uint32_t*>(win + s_at[j]) >> (16 * h);
+      }
+      bf16x8_t a[2][4], b[2][2];
+      lm_read_a(a[0], st, 0, wm, lane);
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int row = row0 + wm * 128 + i * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-          if (row < row_end && col < N) {
-            const float v = gv * acc[i][j][e];
-            if (p.out_f32)
-              reinterpret_cast<float*>(p.y)[(int64_t)row * N + col] = v;
-            else
-              reinterpret_cast<uint16_t*>(p.y)[(int64_t)row * N + col] =
-                  (uint16_t)float_to_bf16_rne(v);
+      for (int j = 0; j < 2; ++j) b[0][j] = dequant8(wd[j][0], decode_e4m3<0>(sc[j]));
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        if (ks + 1 < 4) lm_read_a(a[(ks + 1) & 1], st, ks + 1, wm, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks & 1][i], b[ks & 1][j],
+                                                                acc[i][j], 0, 0, 0);
+        if (ks + 1 < 4) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            b[(ks + 1) & 1][j] = dequant8(wd[j][ks + 1], ((ks + 1) >> 1) ? decode_e4m3<1>(sc[j])
+                                                                         : decode_e4m3<0>(sc[j]));
+        }
+        // one activation load per sub-step (bunched, they held the wave
+        // longer at the load path)
+        if (ks == 0 && prew) lm_issue_w(ring0, s + 2, rw, rs, off, wave);
+        if (prex) lm_issue_x(ring0, s + 3, ks, rx, off, wave);
+      }
+    }
+    __syncthreads();  // every wave's fragment reads done: the ring is free
+
+    if (vec_out) {
+      // epilogue through a per-wave 32 x 32 FP32 scratch tile: lane l of
+      // tile (i, j) holds column l % 32 and rows 8 (e / 4) + 4 (l / 32) + e % 4;
+      // read back, lane l takes row l / 2, columns 16 (l % 2) .. + 15, and
+      // writes them as whole 16-byte pieces
+      float* scr = reinterpret_cast<float*>(ring + wave * L::kEpiBytes);
+      const int rr = lane >> 1, hh = lane & 1;
+      const int row_bytes = N * ob;
+      const __amdgpu_buffer_rsrc_t ry =
+          make_rsrc(static_cast<const char*>(p.y) + (int64_t)row0 * row_bytes,
+                    (uint32_t)((row_end - row0) * row_bytes));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) scr[(8 * (e >> 2) + 4 * h + (e & 3)) * 32 + r32] = acc[i][j][e];
+          f32x4_t v[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            v[c] = *reinterpret_cast<const f32x4_t*>(scr + rr * 32 + 16 * hh + 4 * c);
+          const int row = wm * 128 + i * 32 + rr;  // within the tile
+          const int col = n0 + wn * 64 + j * 32 + 16 * hh;
+          const bool ok = row0 + row < row_end && col < N;
+          const uint32_t o = ok ? (uint32_t)(row * row_bytes + col * ob) : kOffNone;
+          if (p.out_f32) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              __builtin_amdgcn_raw_buffer_store_b128(
+                  __builtin_bit_cast(u32x4_t, f32x4_t{gv * v[c][0], gv * v[c][1], gv * v[c][2],
+                                                      gv * v[c][3]}),
+                  ry, o + (ok ? 16 * c : 0), 0, 0);
+          } else {
+            uint32_t w[8];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              w[2 * c] = float_to_bf16_rne(gv * v[c][0]) | (float_to_bf16_rne(gv * v[c][1]) << 16);
+              w[2 * c + 1] = float_to_bf16_rne(gv * v[c][2]) | (float_to_bf16_rne(gv * v[c][3]) << 16);
+            }
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{w[0], w[1], w[2], w[3]}, ry, o, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{w[4], w[5], w[6], w[7]}, ry,
+                                                   o + (ok ? 16 : 0), 0, 0);
           }
         }
-      }
+      __syncthreads();  // scratch reads done before the next tile's loads land
+    } else {
+      // lane l of tile (i, j) holds column l % 32 and rows
+      // 8 (e / 4) + 4 (l / 32) + e % 4 of the 32 x 32 block
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int col = n0 + wn * 64 + j * 32 + r32;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int row = row0 + wm * 128 + i * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+            if (row < row_end && col < N) {
+              const float v = gv * acc[i][j][e];
+              if (p.out_f32)
+                reinterpret_cast<float*>(p.y)[(int64_t)row * N + col] = v;
+              else
+                reinterpret_cast<uint16_t*>(p.y)[(int64_t)row * N + col] =
+                    (uint16_t)float_to_bf16_rne(v);
+            }
+          }
+        }
+    }
   }
 }
 
@@ -1714,13 +1736,17 @@ static int env_int(const char* name, int dflt) {
 constexpr int kLmMinRows = 256;
 constexpr int kMinSplitStages = 7;
 
-static void choose_kernel(GemmPlan& pl, int64_t rows, int64_t n, bool grouped, int cu_count) {
+static void choose_kernel(GemmPlan& pl, int64_t rows, int64_t n, int64_t k, bool grouped,
+                          int cu_count) {
   // the large-M kernel has no K split: it needs a 256 x 256 output tile for
   // every CU (at N = 4096, K = 7168 it is 1.2-5x slower than the 64-row
   // K-phase kernel with split K from 256 to 2048 rows, and faster at 4096)
   const int64_t lm_tiles = ((rows + kLmBM - 1) / kLmBM) * ((n + kLmBN - 1) / kLmBN);
   const int lm = env_int("NVFP4_LM", 1);  // 0: never, 2: whenever the shape allows
-  if (pl.fast && !grouped && rows >= kLmMinRows && lm != 0 && (lm == 2 || lm_tiles >= cu_count)) {
+  // (its buffer offsets address a 256-row activation tile in 31 bits)
+  const bool lm_fits = (int64_t)kLmBM * 2 * k < ((int64_t)1 << 31);
+  if (pl.fast && !grouped && rows >= kLmMinRows && lm != 0 && lm_fits &&
+      (lm == 2 || lm_tiles >= cu_count)) {
     pl.kind = 3; pl.bn = kLmBN; pl.bm = kLmBM;
   } else if (!pl.fast) {
     pl.kind = 0; pl.bn = 256; pl.nslot = 0;
@@ -1854,7 +1880,7 @@ GemmPlan plan_gemm(int64_t rows, int64_t num_experts, int64_t n, int64_t k, bool
   const int force_bm = env_int("NVFP4_BM", 0);
   if (force_bm == 16 || force_bm == 32 || force_bm == 64) bm = force_bm;
   pl.bm = bm;
-  choose_kernel(pl, rows, n, grouped, cu_count);
+  choose_kernel(pl, rows, n, k, grouped, cu_count);
   // the large-M kernel keeps no schedule (dense only)
   pl.dyn_lds = pl.kind == 3 ? 0 : sched_lds_bytes(grouped ? num_experts : 1);
   bm = pl.bm;

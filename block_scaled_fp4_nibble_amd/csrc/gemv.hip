@@ -430,48 +430,62 @@ __global__ __launch_bounds__(kGemvThreads) void decode_sk_kernel(GemmParams p) {
     }
   }
 
-  // sum the waves in a fixed order: w += w + 4 (w < 4), then wave 0 adds
-  // waves 1, 2, 3
+  // Sum the waves in a fixed order, (((w0 + w4) + (w1 + w5)) + (w2 + w6)) +
+  // (w3 + w7): waves 4..7 hand their sums to waves 0..3, which publish the
+  // four pair sums, and then every thread adds the four, in that order, for
+  // its share of the tile (float4 q = (f CT + ct) 64 + lane of the
+  // accumulator layout) -- all 512 threads at once, not one wave.
+  constexpr int Q = NF * CT * kWave;                            // float4 values per tile
+  constexpr int QPT = (Q + kGemvThreads - 1) / kGemvThreads;    // per thread: 1 or 2
   f32x4_t* xch = reinterpret_cast<f32x4_t*>(xs);
   auto put = [&](int slot) {
 #pragma unroll
     for (int f = 0; f < NF; ++f)
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) xch[((slot * NF + f) * CT + ct) * kWave + lane] = acc[f][ct];
-  };
-  auto add = [&](int slot) {
-#pragma unroll
-    for (int f = 0; f < NF; ++f)
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
-        acc[f][ct] = acc[f][ct] + xch[((slot * NF + f) * CT + ct) * kWave + lane];
+      for (int ct = 0; ct < CT; ++ct) xch[slot * Q + (f * CT + ct) * kWave + lane] = acc[f][ct];
   };
   __syncthreads();
   if (wave >= 4) put(wave - 4);
   __syncthreads();
-  if (wave < 4) add(wave);
-  __syncthreads();
-  if (wave >= 1 && wave < 4) put(wave);
-  __syncthreads();
-  if (wave == 0) {
-    add(1);
-    add(2);
-    add(3);
+  if (wave < 4) {
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+        acc[f][ct] = acc[f][ct] + xch[wave * Q + (f * CT + ct) * kWave + lane];
+    put(wave);
   }
+  __syncthreads();
+  f32x4_t sum[QPT];
+#pragma unroll
+  for (int i = 0; i < QPT; ++i) {
+    const int q = tid + i * kGemvThreads;
+    if (q < Q) sum[i] = ((xch[q] + xch[Q + q]) + xch[2 * Q + q]) + xch[3 * Q + q];
+  }
+  // float4 q of the accumulator layout -> its 4 elements of the row-major
+  // FP32 tile in LDS (rows 16 f + 4 g + r, column 16 ct + l % 16)
+  float* tile = reinterpret_cast<float*>(xs);  // [BM][kDskCols]
+  const float gv = p.g[0];
+  auto to_tile = [&](int q, const f32x4_t& v) {
+    const int slot = q / kWave, l = q % kWave;
+    const int f = slot / CT, ct = slot % CT;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      tile[(16 * f + 4 * (l >> 4) + r) * kDskCols + 16 * ct + (l & 15)] = gv * v[r];
+  };
   const int S = p.splits;
   if (S > 1) {
+    // every thread stores its share of the partial tile (device-scope
+    // stores), waits for them, and one thread counts the arrival
     const __amdgpu_buffer_rsrc_t part =
         dsk_rsrc(p.partials + (int64_t)nt * S * (BM * kDskCols), (uint32_t)(S * BM * kDskCols * 4));
-    auto poff = [&](int ss, int f, int ct) {
-      return (uint32_t)((ss * (BM * kDskCols) + ((f * CT + ct) * kWave + lane) * 4) * 4);
-    };
-    if (wave == 0) {
+    auto poff = [&](int ss, int q) { return (uint32_t)((ss * (BM * kDskCols) + 4 * q) * 4); };
 #pragma unroll
-      for (int f = 0; f < NF; ++f)
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, acc[f][ct]), part,
-                                                 poff(s, f, ct), 0, kDskCpol);
+    for (int i = 0; i < QPT; ++i) {
+      const int q = tid + i * kGemvThreads;
+      if (q < Q)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, sum[i]), part,
+                                               poff(s, q), 0, kDskCpol);
     }
     __builtin_amdgcn_s_waitcnt(0);  // the partial stores have completed
     __syncthreads();
@@ -483,49 +497,40 @@ __global__ __launch_bounds__(kGemvThreads) void decode_sk_kernel(GemmParams p) {
     __syncthreads();
     if (!last_flag) return;  // uniform: another split finishes the tile
     // The last split sums all S partial tiles (its own included, as stored)
-    // in split order.  The tile's NF x CT accumulator slots are dealt out to
-    // the 8 waves, and each wave issues the loads of up to 8 splits before it
-    // adds any, so the hand-off costs a few memory latencies, not S of them.
-    constexpr int SLOTS = NF * CT;                            // 4 .. 16
-    constexpr int SPW = (SLOTS + kGemvWaves - 1) / kGemvWaves;  // slots per wave
-    constexpr int U = 8;                                      // splits in flight
-    float* tile = reinterpret_cast<float*>(xs);               // [BM][kDskCols]
-    const float gv = p.g[0];
+    // in split order, each thread for its share; the loads of up to U splits
+    // of all its shares are in flight before it adds any, so the hand-off
+    // costs one memory latency per U splits.
+    constexpr int U = 8;
+    f32x4_t tot[QPT];
+    for (int s0 = 0; s0 < S; s0 += U) {
+      f32x4_t v[QPT][U];
 #pragma unroll
-    for (int q = 0; q < SPW; ++q) {
-      const int slot = wave + kGemvWaves * q;
-      if (slot >= SLOTS) break;  // wave-uniform
-      const int f = slot / CT, ct = slot % CT;
-      f32x4_t sum = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      for (int s0 = 0; s0 < S; s0 += U) {
-        f32x4_t v[U];
+      for (int i = 0; i < QPT; ++i) {
+        const int q = tid + i * kGemvThreads;
 #pragma unroll
-        for (int i = 0; i < U; ++i)
-          v[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                 part, s0 + i < S ? poff(s0 + i, f, ct) : kDskOffNone,
-                                                 0, kDskCpol));
-#pragma unroll
-        for (int i = 0; i < U; ++i)
-          if (s0 + i < S) sum = (s0 + i == 0) ? v[i] : sum + v[i];
+        for (int u = 0; u < U; ++u)
+          v[i][u] = __builtin_bit_cast(
+              f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                           part, (q < Q && s0 + u < S) ? poff(s0 + u, q) : kDskOffNone, 0, kDskCpol));
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        tile[(16 * f + 4 * g + r) * kDskCols + 16 * ct + c16] = gv * sum[r];
+      for (int i = 0; i < QPT; ++i)
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (s0 + u < S) tot[i] = (s0 + u == 0) ? v[i][u] : tot[i] + v[i][u];
+    }
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+      const int q = tid + i * kGemvThreads;
+      if (q < Q) to_tile(q, tot[i]);
     }
     if (tid == 0) __hip_atomic_store(&p.counters[nt], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   } else {
-    // one split: wave 0 holds the whole sum; lay it out row-major in LDS
-    float* tile = reinterpret_cast<float*>(xs);  // [BM][kDskCols]
-    __syncthreads();  // the exchange slots are free
-    if (wave == 0) {
-      const float gv = p.g[0];
+    __syncthreads();  // every exchange read is done: the tile may overwrite the slots
 #pragma unroll
-      for (int f = 0; f < NF; ++f)
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            tile[(16 * f + 4 * g + r) * kDskCols + 16 * ct + c16] = gv * acc[f][ct][r];
+    for (int i = 0; i < QPT; ++i) {
+      const int q = tid + i * kGemvThreads;
+      if (q < Q) to_tile(q, sum[i]);
     }
   }
   // Output: the tile is row-major in LDS (FP32, g applied); every thread
@@ -533,7 +538,6 @@ __global__ __launch_bounds__(kGemvThreads) void decode_sk_kernel(GemmParams p) {
   // instead of one 2- or 4-byte store per element -- and only the pieces
   // that reach past column N, or whose rows are not 16-byte aligned, go
   // element by element.
-  const float* tile = reinterpret_cast<const float*>(xs);
   __syncthreads();
   const int esz = p.out_f32 ? 4 : 2;
   const int cpr = kDskCols * esz / 16;  // 16-byte pieces per tile row

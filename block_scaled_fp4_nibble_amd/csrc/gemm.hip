@@ -305,6 +305,18 @@ __device__ __forceinline__ int round_unit(int round, int w, int G) {
   return round * G + in_round;
 }
 
+// The K-phase kernel's units are sorted by cost (the experts with the most
+// rows first), so a plain round-robin hands workgroup 0 the costliest unit
+// of every round and the last workgroup the cheapest.  Odd rounds therefore
+// take the round's ids in reverse order (each XCD's block of ids stays
+// contiguous), which evens out the workgroups' totals (1-2 % on the MoE
+// launches; what remains idle at their end is the last, partly filled
+// round, not the cost order).
+__device__ __forceinline__ int snake_unit(int round, int w, int G) {
+  const int in_round = (G % 8 == 0) ? (w % 8) * (G / 8) + w / 8 : w;
+  return round * G + ((round & 1) ? G - 1 - in_round : in_round);
+}
+
 // Units of expert e are ordered (column tile, split, row tile); the expert's
 // output tiles (for the split-K counters) are numbered units / splits.
 // P2: the second product of a fused launch, whose units (p.n_tiles column
@@ -1051,10 +1063,10 @@ __device__ __forceinline__ void kp_units(const GemmParams& p, Sched& sc, uint8_t
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int kp = wave & 1, ch = wave >> 1;
   const int G = gridDim.x;
-  // the workgroup's units are round_unit(round, blockIdx.x, G) for rounds
+  // the workgroup's units are snake_unit(round, blockIdx.x, G) for rounds
   // while the unit id is below total (the grid may exceed the unit count of
   // a grouped product, and the map permutes workgroups within a round)
-  const int first = round_unit(0, blockIdx.x, G);
+  const int first = snake_unit(0, blockIdx.x, G);
   if (total <= 0 || first >= total) return;
   const KpOffsets<BM, KW, BN> off = kp_offsets<BM, NSLOT, KW, BN>(p.k, wave, lane);
   // the epilogue goes through LDS (a fixed number of 16-byte stores) when
@@ -1078,7 +1090,7 @@ __device__ __forceinline__ void kp_units(const GemmParams& p, Sched& sc, uint8_t
   int sb0 = 0, wb0 = 0, pf = 0;
   bool ex = false;
   for (;;) {
-    const int nu = round_unit(round + 1, blockIdx.x, G);
+    const int nu = snake_unit(round + 1, blockIdx.x, G);
     const bool has_next = nu < total;
     Unit un = u;
     KpU nx = cu;
@@ -1258,6 +1270,10 @@ __global__ __launch_bounds__(KW * 64) void gemm_kp_kernel(GemmParams p) {
 // LDS rows of the activation tile keep their 16-byte chunk c in slot
 // c ^ ((r >> 1) & 7), so the 32-row fragment reads spread over all banks.
 constexpr int kLmBM = 256, kLmBN = 256, kLmBK = 64;
+// waves per workgroup split as kLmWM row groups x kLmWN column groups
+constexpr int kLmWN = 4, kLmWM = 8 / kLmWN;
+constexpr int kLmRW = kLmBM / kLmWM, kLmCW = kLmBN / kLmWN;  // rows, columns per wave
+constexpr int kLmNI = kLmRW / 32, kLmNJ = kLmCW / 32;         // 32 x 32 tiles per wave
 
 struct LmLayout {
   static constexpr int kWaves = 8;
@@ -1325,13 +1341,13 @@ __device__ __forceinline__ void lm_issue_x(uint32_t ring0, int step, int tt, u32
   lds_dma16(st + (wave * LmLayout::kXLoads + tt) * 1024, o.x[tt], (uint32_t)(step * kLmBK * 2), rx);
 }
 
-// Activation fragments of sub-step ks: 4 row tiles of the wave's 128 rows.
-__device__ __forceinline__ void lm_read_a(bf16x8_t (&a)[4], const uint8_t* st, int ks, int wm,
+// Activation fragments of sub-step ks: the row tiles of the wave's rows.
+__device__ __forceinline__ void lm_read_a(bf16x8_t (&a)[kLmNI], const uint8_t* st, int ks, int wm,
                                           int lane) {
   const int r32 = lane & 31, h = lane >> 5;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    a[i] = *reinterpret_cast<const bf16x8_t*>(st + lm_swz(wm * 128 + i * 32 + r32, 4 * h + ks));
+  for (int i = 0; i < kLmNI; ++i)
+    a[i] = *reinterpret_cast<const bf16x8_t*>(st + lm_swz(wm * kLmRW + i * 32 + r32, 4 * h + ks));
 }
 
 // Dense only (offsets == nullptr, one expert): tile t of the grid is
@@ -1341,7 +1357,7 @@ __global__ __launch_bounds__(LmLayout::kWaves * 64) void gemm_lm_kernel(GemmPara
   __shared__ __attribute__((aligned(16))) uint8_t ring[L::kTotal];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave >> 2, wn = wave & 3;  // 128-row half, 64-column quarter
+  const int wm = wave / kLmWN, wn = wave % kLmWN;  // row group, column group
   const int r32 = lane & 31, h = lane >> 5;
   const int N = p.n, K = p.k;
   const int m_tiles = (int)((p.rows + kLmBM - 1) / kLmBM);
@@ -1357,11 +1373,11 @@ __global__ __launch_bounds__(LmLayout::kWaves * 64) void gemm_lm_kernel(GemmPara
   const bool vec_out = N % 16 == 0 && (int64_t)kLmBM * N * ob < ((int64_t)1 << 31);
   // the lane's weight bytes within a weight slot and its scales within a
   // window, per column tile j
-  uint32_t wp_at[2], s_at[2];
+  uint32_t wp_at[kLmNJ], s_at[kLmNJ];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    wp_at[j] = (uint32_t)((wn * 64 + j * 32 + r32) * 32 + 16 * h);
-    s_at[j] = (uint32_t)((wn * 64 + j * 32 + r32) * 16);
+  for (int j = 0; j < kLmNJ; ++j) {
+    wp_at[j] = (uint32_t)((wn * kLmCW + j * 32 + r32) * 32 + 16 * h);
+    s_at[j] = (uint32_t)((wn * kLmCW + j * 32 + r32) * 16);
   }
 
   for (int round = 0; round * (int)gridDim.x < total; ++round) {
@@ -1376,11 +1392,11 @@ __global__ __launch_bounds__(LmLayout::kWaves * 64) void gemm_lm_kernel(GemmPara
     const u32x4_t rs = rsrc_words(p.s + (int64_t)n0 * (K / 16),
                                   (uint32_t)(min(N - n0, kLmBN)) * (uint32_t)(K / 16));
 
-    f32x16_t acc[4][2];
+    f32x16_t acc[kLmNI][kLmNJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kLmNI; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < kLmNJ; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
@@ -1414,29 +1430,29 @@ __global__ __launch_bounds__(LmLayout::kWaves * 64) void gemm_lm_kernel(GemmPara
       const uint8_t* win = ring + L::kWin + ((s / L::kWinSteps) & 1) * L::kWinBytes +
                            4 * (s % L::kWinSteps);
       const bool prew = s + 2 < nsteps, prex = s + 3 < nsteps;
-      u32x4_t wd[2];
-      uint32_t sc[2];
+      u32x4_t wd[kLmNJ];
+      uint32_t sc[kLmNJ];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < kLmNJ; ++j) {
         wd[j] = *reinterpret_cast<const u32x4_t*>(wst + wp_at[j]);
         sc[j] = *reinterpret_cast<const uint32_t*>(win + s_at[j]) >> (16 * h);
       }
-      bf16x8_t a[2][4], b[2][2];
+      bf16x8_t a[2][kLmNI], b[2][kLmNJ];
       lm_read_a(a[0], st, 0, wm, lane);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) b[0][j] = dequant8(wd[j][0], decode_e4m3<0>(sc[j]));
+      for (int j = 0; j < kLmNJ; ++j) b[0][j] = dequant8(wd[j][0], decode_e4m3<0>(sc[j]));
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         if (ks + 1 < 4) lm_read_a(a[(ks + 1) & 1], st, ks + 1, wm, lane);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < kLmNI; ++i)
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
+          for (int j = 0; j < kLmNJ; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks & 1][i], b[ks & 1][j],
                                                                 acc[i][j], 0, 0, 0);
         if (ks + 1 < 4) {
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
+          for (int j = 0; j < kLmNJ; ++j)
             b[(ks + 1) & 1][j] = dequant8(wd[j][ks + 1], ((ks + 1) >> 1) ? decode_e4m3<1>(sc[j])
                                                                          : decode_e4m3<0>(sc[j]));
         }
@@ -1460,17 +1476,17 @@ __global__ __launch_bounds__(LmLayout::kWaves * 64) void gemm_lm_kernel(GemmPara
           make_rsrc(static_cast<const char*>(p.y) + (int64_t)row0 * row_bytes,
                     (uint32_t)((row_end - row0) * row_bytes));
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kLmNI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < kLmNJ; ++j) {
 #pragma unroll
           for (int e = 0; e < 16; ++e) scr[(8 * (e >> 2) + 4 * h + (e & 3)) * 32 + r32] = acc[i][j][e];
           f32x4_t v[4];
 #pragma unroll
           for (int c = 0; c < 4; ++c)
             v[c] = *reinterpret_cast<const f32x4_t*>(scr + rr * 32 + 16 * hh + 4 * c);
-          const int row = wm * 128 + i * 32 + rr;  // within the tile
-          const int col = n0 + wn * 64 + j * 32 + 16 * hh;
+          const int row = wm * kLmRW + i * 32 + rr;  // within the tile
+          const int col = n0 + wn * kLmCW + j * 32 + 16 * hh;
           const bool ok = row0 + row < row_end && col < N;
           const uint32_t o = ok ? (uint32_t)(row * row_bytes + col * ob) : kOffNone;
           if (p.out_f32) {
@@ -1497,13 +1513,13 @@ __global__ __launch_bounds__(LmLayout::kWaves * 64) void gemm_lm_kernel(GemmPara
       // lane l of tile (i, j) holds column l % 32 and rows
       // 8 (e / 4) + 4 (l / 32) + e % 4 of the 32 x 32 block
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kLmNI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int col = n0 + wn * 64 + j * 32 + r32;
+        for (int j = 0; j < kLmNJ; ++j) {
+          const int col = n0 + wn * kLmCW + j * 32 + r32;
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
-            const int row = row0 + wm * 128 + i * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+            const int row = row0 + wm * kLmRW + i * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
             if (row < row_end && col < N) {
               const float v = gv * acc[i][j][e];
               if (p.out_f32)

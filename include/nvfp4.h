@@ -194,8 +194,10 @@ nvfp4_status_t nvfp4_grouped_gemm_gather(const void* x_bf16, int64_t x_rows,
  * gate_up GEMM, SiLU and the down GEMM into a single persistent kernel):
  *   h = nvfp4_grouped_gemm_swiglu(x, up weights)      h [rows][d_ff]
  *   y = nvfp4_grouped_gemm(h, down weights)           y [rows][d_model]
- * over the same expert segments, with the results of those two calls (bit
- * for bit: the same kernels and summation order).  x [rows][d_model] holds
+ * over the same expert segments.  Neither product splits K here, so h and
+ * y equal, bit for bit, what those two calls return when their schedules do
+ * not split K either (the same kernels and summation order); a K split there
+ * sums in another order, within the same error bound.  x [rows][d_model] holds
  * the routed rows sorted by expert; up_packed[e] [2 d_ff][d_model/2] (32-row
  * gate/up groups, as for nvfp4_grouped_gemm_swiglu), up_scales, up_global[e];
  * down_packed[e] [d_model][d_ff/2], down_scales, down_global[e].  h (caller-
@@ -206,10 +208,10 @@ nvfp4_status_t nvfp4_grouped_gemm_gather(const void* x_bf16, int64_t x_rows,
  * sized so that all workgroups are resident; should one wait time out anyway
  * (another kernel holding CUs), NVFP4_DSTATUS_WAIT_TIMEOUT is set, that
  * workgroup stops waiting, and y is unspecified.
- * Requirements: d_ff % 16 == 0, d_model % 64 == 0 and d_ff % 64 == 0, and a
- * schedule in which both products take the same K-phase kernel with no K
- * split; otherwise NVFP4_ERR_UNSUPPORTED and nothing is enqueued (the two
- * calls above then compute the same result).  Workspace:
+ * Requirements: d_model % 64 == 0, d_ff % 64 == 0, 2 d_ff and d_model at most
+ * 2^23, and a schedule in which both products take the same K-phase kernel
+ * configuration; otherwise NVFP4_ERR_UNSUPPORTED and nothing is enqueued (the
+ * two calls above then compute the result).  Workspace:
  * nvfp4_grouped_mlp_workspace_size() bytes; the call zeroes its per-row-tile
  * counts (after the first nvfp4_workspace_counter_bytes(), which it never
  * touches) on `stream`, so the buffer may also serve the GEMM calls.

@@ -1241,11 +1241,13 @@ __global__ __launch_bounds__(KW * 64) void gemm_kp_kernel(GemmParams p) {
 //
 // For a dense product with at least a few hundred rows a 256 x 256 output
 // tile per workgroup of 8 waves amortizes the activation and weight traffic:
-// wave w = (wm, wn) computes rows [128 wm, 128 wm + 128) x columns
-// [64 wn, 64 wn + 64) of the tile as 4 x 2 v_mfma_f32_32x32x16_bf16 tiles
-// (FP32 accumulators).  Two waves share each SIMD, so one wave's
-// dequantization and load issue run while the other's MFMAs occupy the
-// matrix pipeline.  K advances in 64-wide steps.  LDS holds a 4-slot ring of
+// wave w computes all 256 rows x columns [32 w, 32 w + 32) of the tile as
+// 8 x 1 v_mfma_f32_32x32x16_bf16 tiles (FP32 accumulators), so every weight
+// of the tile is dequantized by one wave only (two waves sharing a column
+// range, each on half of the rows, both dequantized it: 2-4 % slower at
+// 8192^3), at the price of reading each activation fragment from LDS in all
+// eight waves.  Two waves share each SIMD, so one wave's dequantization and
+// load issue run while the other's MFMAs occupy the matrix pipeline.  K advances in 64-wide steps.  LDS holds a 4-slot ring of
 // activation tiles (256 rows x 128 B), a 3-slot ring of packed weight tiles
 // (256 rows x 32 B, only the 4.5-bit data) and two windows of block scales
 // covering 4 steps each (256 rows x 16 B, one 16-byte load per row: a load
@@ -1258,9 +1260,8 @@ __global__ __launch_bounds__(KW * 64) void gemm_kp_kernel(GemmParams p) {
 // of them; three steps of lead hide that latency where two did not (8192^3:
 // 941 -> 848 us in a timing copy).  Weight lines (128 B = four steps of a
 // row) miss once in four steps, and two steps of lead cover them.  Each wave
-// dequantizes its own 64 columns of the step from the packed bytes in
-// registers; the two waves sharing a column range both do, which costs VALU
-// time the MFMAs of the other wave hide, and keeps BF16 weights out of LDS.
+// dequantizes its own 32 columns of the step from the packed bytes in
+// registers, which keeps BF16 weights out of LDS.
 //
 // K slots: in sub-step ks (16 K) of a step, lane l (row / column l % 32,
 // half h = l / 32) supplies K = 32 h + 8 ks .. + 7 of the step, for both
@@ -1271,7 +1272,7 @@ __global__ __launch_bounds__(KW * 64) void gemm_kp_kernel(GemmParams p) {
 // c ^ ((r >> 1) & 7), so the 32-row fragment reads spread over all banks.
 constexpr int kLmBM = 256, kLmBN = 256, kLmBK = 64;
 // waves per workgroup split as kLmWM row groups x kLmWN column groups
-constexpr int kLmWN = 4, kLmWM = 8 / kLmWN;
+constexpr int kLmWN = 8, kLmWM = 8 / kLmWN;
 constexpr int kLmRW = kLmBM / kLmWM, kLmCW = kLmBN / kLmWN;  // rows, columns per wave
 constexpr int kLmNI = kLmRW / 32, kLmNJ = kLmCW / 32;         // 32 x 32 tiles per wave
 

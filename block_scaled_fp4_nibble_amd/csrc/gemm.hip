@@ -21,7 +21,10 @@
 //    column tile of BN weight rows, K split).  Every workgroup reads the
 //    expert offsets from device memory, builds the per-expert unit prefix in
 //    LDS and walks units in XCD-aware rounds.  Empty experts own no units.
-//    There is no host synchronization and no inter-workgroup wait.
+//    There is no host synchronization.  Workgroups wait for each other only
+//    in the fused MoE MLP launch (a down-projection unit waits, with a
+//    bounded poll, for the gate_up tiles of its rows) and in the split-K
+//    hand-off (the last split to arrive finishes the tile; nobody waits).
 //  - MFMA v_mfma_f32_16x16x32_bf16.  Operand A = activations (16 rows),
 //    operand B = dequantized weights (16 weight rows = 16 output columns).
 //    Lane l holds row/column l % 16 and 8 consecutive K of lane group
@@ -38,6 +41,9 @@
 //    column slice and one K half of every stage; row fragments that hold
 //    only padding rows of a tile are skipped (the K loop is instantiated per
 //    number of occupied fragments).  Details at the kernel.
+//  - Large-M kernel (dense, k % 64 == 0, hundreds of rows): 256 x 256 tiles,
+//    v_mfma_f32_32x32x16_bf16, each wave on all 256 rows of 32 columns.
+//    Details at the kernel.
 //  - Register kernel (any k % 16 == 0): 4 waves x 64 columns, weights loaded
 //    straight into registers one 256-wide chunk ahead, activations staged
 //    through a double-buffered LDS tile.

@@ -17,6 +17,87 @@ typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 
 constexpr int kWave = 64;
 
+// Direct global -> LDS loads (buffer_load ... lds): lane l writes its bytes
+// at M0 + l * size.  They are issued from inline assembly so that the
+// compiler does not treat every later LDS read as a possible alias of an
+// in-flight load and wait for all of them (which would serialize a ring of
+// stages); the kernels wait for exactly the loads they need with explicit
+// vmcnt waits.  M0 is saved and restored around each load.
+__device__ __forceinline__ u32x4_t rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4_t{(uint32_t)a, (uint32_t)(a >> 32), bytes, 0x00020000u};
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)(p);
+}
+
+// COH: a device-coherent load (sc1), for data another XCD wrote during the
+// same launch (which this XCD's L2 may hold stale).
+template <bool COH = false>
+__device__ __forceinline__ void lds_dma16(uint32_t lds, uint32_t voff, uint32_t soff,
+                                          u32x4_t rsrc) {
+  // the descriptor is uniform; say so, so that it stays in SGPRs
+  rsrc = u32x4_t{(uint32_t)__builtin_amdgcn_readfirstlane(rsrc[0]),
+                 (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[1]),
+                 (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[2]),
+                 (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[3])};
+  uint32_t saved;
+  if constexpr (COH)
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "buffer_load_dwordx4 %2, %3, %4 offen sc1 lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc),
+          "s"(__builtin_amdgcn_readfirstlane(soff))
+        : "memory");
+  else
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc),
+          "s"(__builtin_amdgcn_readfirstlane(soff))
+        : "memory");
+}
+
+// s_waitcnt vmcnt(n) for a run-time n: the immediate must be a constant.
+// Encoding (gfx9): vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt
+// and lgkmcnt left at their maxima (no wait on them).  n >= 63 needs no
+// wait (the counter cannot exceed 63); n <= 0 waits for everything.
+__device__ __forceinline__ void wait_vmcnt(int n) {
+#define NVFP4_VMCNT(v) \
+  case v: __builtin_amdgcn_s_waitcnt(((v) & 15) | (((v) >> 4) << 14) | (7 << 4) | (15 << 8)); break;
+#define NVFP4_VMCNT8(b) NVFP4_VMCNT(b) NVFP4_VMCNT(b + 1) NVFP4_VMCNT(b + 2) NVFP4_VMCNT(b + 3) \
+  NVFP4_VMCNT(b + 4) NVFP4_VMCNT(b + 5) NVFP4_VMCNT(b + 6) NVFP4_VMCNT(b + 7)
+  if (n >= 63) return;
+  switch (n) {
+    NVFP4_VMCNT8(8) NVFP4_VMCNT8(16) NVFP4_VMCNT8(24) NVFP4_VMCNT8(32) NVFP4_VMCNT8(40)
+    NVFP4_VMCNT8(48) NVFP4_VMCNT(1) NVFP4_VMCNT(2) NVFP4_VMCNT(3) NVFP4_VMCNT(4)
+    NVFP4_VMCNT(5) NVFP4_VMCNT(6) NVFP4_VMCNT(7) NVFP4_VMCNT(56) NVFP4_VMCNT(57)
+    NVFP4_VMCNT(58) NVFP4_VMCNT(59) NVFP4_VMCNT(60) NVFP4_VMCNT(61) NVFP4_VMCNT(62)
+    default: __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8)); break;
+  }
+#undef NVFP4_VMCNT8
+#undef NVFP4_VMCNT
+}
+
+// s_waitcnt lgkmcnt(0): this wave's LDS (and scalar) accesses have completed.
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+}
+
+// s_waitcnt vmcnt(N) for a compile-time N.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_c() {
+  static_assert(N >= 0 && N < 63, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // Largest finite E4M3 (OCP FN) value and the E2M1 maximum; the tensor-level
 // divisor is their product.
 constexpr float kE4M3Max = 448.0f;

@@ -268,21 +268,28 @@ __global__ __launch_bounds__(kGemvThreads) void decode_mfma_kernel(GemmParams p)
 // count chosen so that the units about fill the CUs (N = 4096, K = 7168: 64
 // column tiles x 4 splits).  Wave w of the 8 owns the unit's 128-deep K groups
 // j with j % 8 == w, for all four 16-column tiles, so every activation
-// fragment it reads from LDS feeds four MFMAs.  Each lane first loads the
-// first phase of the token rows, then issues every weight load of its share
-// -- per group and column tile 16 bytes of its weight row at K = 128 j +
-// 32 (l / 16) and the two scale bytes, the K-slot permutation of
-// decode_mfma_kernel.  The token rows (split K range, all rows) go through
-// registers into LDS in phases of up to kDskPhase<NF> groups, each row's
-// 16-byte chunk c at c ^ (row % 16); with up to 32 rows the next phase's
-// loads are in flight while this phase is multiplied out.  The waves' sums meet through LDS in a
-// fixed order, the splits of a column tile through device-scope partial tiles
-// and an arrival counter, and the last split sums them in split order (so the
-// result does not depend on timing).
-constexpr int kDskXBytes = 120 * 1024;  // LDS for one phase of token rows
+// fragment it reads from LDS feeds four MFMAs.  Only wave w reads the token
+// rows of its groups, so they go straight from memory (buffer_load ... lds)
+// into a region of LDS of its own, and each wave waits for its own loads
+// only: no barrier stands between the loads and the MFMAs.  Each wave first
+// issues the token rows of its first group (of both, when 8 waves x 2 groups
+// fit the LDS, up to 32 rows), then every weight load of its share -- per
+// group and column tile 16 bytes of its weight row at K = 128 j + 32 (l / 16)
+// and the two scale bytes, the K-slot permutation of decode_mfma_kernel.
+// With more rows its second group's token rows replace the first's once that
+// group is multiplied out.  A row's 16-byte chunk c sits at c ^ (row % 16).
+// (Staged through registers into one shared LDS tile in phases of groups,
+// with a barrier per phase, the launch took 6-10 % longer at 16-64 rows.)
+// The waves' sums meet through LDS in a fixed order, the splits of a column
+// tile through device-scope partial tiles and an arrival counter, and the
+// last split sums them in split order (so the result does not depend on
+// timing).
+constexpr int kDskXBytes = 128 * 1024;  // LDS for the waves' token-row regions
+// groups a wave's region holds: both of its groups when they fit, else one
 template <int NF>
-constexpr int kDskPhase = (kDskXBytes / (NF * 16 * 256)) < kDskMaxGroups ? kDskXBytes / (NF * 16 * 256)
-                                                                           : kDskMaxGroups;
+constexpr int kDskRes = kGemvWaves * (kDskMaxGroups / kGemvWaves) * NF * 4096 <= kDskXBytes
+                            ? kDskMaxGroups / kGemvWaves
+                            : 1;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t dsk_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
@@ -296,15 +303,14 @@ template <int NF>
 __global__ __launch_bounds__(kGemvThreads) void decode_sk_kernel(GemmParams p) {
   constexpr int BM = NF * 16;
   constexpr int CT = kDskCols / 16;                  // column tiles per unit
-  constexpr int PG = kDskPhase<NF>;                  // groups per token-row phase
-  constexpr int RCH = PG * 16;                       // 16-byte chunks per staged row
-  constexpr int CPT = (BM * RCH + kGemvThreads - 1) / kGemvThreads;  // chunks per thread
   constexpr int GPW = kDskMaxGroups / kGemvWaves;    // groups per wave (upper bound)
-  constexpr int NPH = (kDskMaxGroups + PG - 1) / PG; // phases (upper bound)
-  constexpr bool kPrefetch = NF <= 2;
+  constexpr int RES = kDskRes<NF>;                   // groups a wave's region holds
+  constexpr int GB = BM * 256;                       // bytes of one group's token rows
+  constexpr int XL = GB / 1024;                      // 1 KB loads per group
   static_assert(kDskCols % 16 == 0 && kDskMaxGroups % kGemvWaves == 0, "unit shape");
-  static_assert((kGemvWaves / 2) * NF * CT * 16 * kWave <= BM * RCH * 16, "exchange fits");
-  __shared__ __attribute__((aligned(16))) uint8_t xs[BM * RCH * 16];
+  static_assert(GPW == 2 && (RES == 1 || RES == GPW), "a wave's groups: one or both resident");
+  static_assert((kGemvWaves / 2) * NF * CT * 16 * kWave <= kGemvWaves * RES * GB, "exchange fits");
+  __shared__ __attribute__((aligned(16))) uint8_t xs[kGemvWaves * RES * GB];
   __shared__ int last_flag;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -320,41 +326,36 @@ __global__ __launch_bounds__(kGemvThreads) void decode_sk_kernel(GemmParams p) {
   const int nrows = min(kDskCols, N - nt * kDskCols);  // weight rows of the unit
   // buffer resources: loads past a resource (rows past N, rows past M, K
   // groups past the unit) read zero, so no load sits behind a branch
-  const __amdgpu_buffer_rsrc_t rx = dsk_rsrc(p.x, (uint32_t)M * (uint32_t)K * 2u);
+  const u32x4_t rxw = rsrc_words(p.x, (uint32_t)M * (uint32_t)K * 2u);
   const __amdgpu_buffer_rsrc_t rw =
       dsk_rsrc(p.w + (int64_t)nt * kDskCols * (K / 2), (uint32_t)(nrows * (K / 2)));
   const __amdgpu_buffer_rsrc_t rs =
       dsk_rsrc(p.s + (int64_t)nt * kDskCols * (K / 16), (uint32_t)(nrows * (K / 16)));
 
-  // token rows of phase `ph` (groups [ph PG, min(ng, ph PG + PG))) into xr
-  u32x4_t xr[CPT];
-  auto load_phase = [&](int ph) {
-    const int gb = ph * PG;
-    const int rc = (min(ng, gb + PG) - gb) * 16;  // chunks per row in this phase
+  // The token rows of group j (all BM rows, 256 bytes each) into slot `sl`
+  // of this wave's region, straight from memory (buffer_load ... lds): load t
+  // covers rows 4t .. 4t + 3, and the 16-byte piece at position q of row r
+  // holds chunk q ^ (r % 16) of the row.  Rows past M and groups past the
+  // unit load zeros.
+  uint8_t* const region = xs + wave * (RES * GB);
+  auto load_group = [&](int j, int sl) {
+    const uint32_t dst = lds_addr(region + sl * GB);
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int ci = tid + i * kGemvThreads;
-      const int row = ci / RCH, c = ci % RCH;
-      const bool ok = row < M && c < rc && ci < BM * RCH;
-      const uint32_t off =
-          ok ? ((uint32_t)row * (uint32_t)K + (uint32_t)(k0 + gb * 128 + 8 * c)) * 2u : kDskOffNone;
-      xr[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
-    }
-  };
-  auto store_phase = [&]() {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int ci = tid + i * kGemvThreads;
-      if (ci < BM * RCH) {
-        const int row = ci / RCH, c = ci % RCH;
-        *reinterpret_cast<u32x4_t*>(xs + (row * RCH + (c ^ (row & 15))) * 16) = xr[i];
-      }
+    for (int t = 0; t < XL; ++t) {
+      const int r = 4 * t + (lane >> 4), q = lane & 15;
+      const int c = q ^ (r & 15);
+      const uint32_t off = (r < M && j < ng)
+                               ? ((uint32_t)r * (uint32_t)K + (uint32_t)(k0 + 128 * j + 8 * c)) * 2u
+                               : kDskOffNone;
+      lds_dma16(dst + t * 1024, off, 0u, rxw);
     }
   };
 
-  // the first token rows go out before the weights (a scheduling fence: no
-  // memory fence, which would make the compiler wait for the loads)
-  load_phase(0);
+  // The wave's first group (both, when they fit) goes out before the weights
+  // (a scheduling fence: no memory fence, which would make the compiler wait
+  // for the loads).
+  load_group(wave, 0);
+  if constexpr (RES == GPW) load_group(wave + kGemvWaves, 1);
   __builtin_amdgcn_sched_barrier(0);
   u32x4_t wv[GPW][CT];
   uint32_t sv[GPW][CT];
@@ -372,63 +373,77 @@ __global__ __launch_bounds__(kGemvThreads) void decode_sk_kernel(GemmParams p) {
     }
   }
   __builtin_amdgcn_sched_barrier(0);
-  store_phase();
-  __syncthreads();
 
   f32x4_t acc[NF][CT];
 #pragma unroll
   for (int f = 0; f < NF; ++f)
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) acc[f][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // step t of group i with its A fragments and the group's weights
+  auto mma_step = [&](int i, int t, const bf16x8_t (&a)[NF]) {
+    bf16x8_t bq[CT];
 #pragma unroll
-  for (int ph = 0; ph < NPH; ++ph) {
-    const int gb = ph * PG;
-    if (gb >= ng) break;  // uniform
-    const bool more = gb + PG < ng;
-    // the next phase's rows are in flight while this one is multiplied out
-    // (with up to 32 rows; above that the registers would not hold them)
-    if (kPrefetch && more) load_phase(ph + 1);
-#pragma unroll
-    for (int i = 0; i < GPW; ++i) {
-      const int j = wave + kGemvWaves * i;
-      if (j < gb || j >= gb + PG || j >= ng) continue;  // wave-uniform
-      const int jj = j - gb;
-      // A fragments of step t + 1 are read while step t is dequantized and
-      // multiplied (LDS latency behind the MFMAs)
-      bf16x8_t a[2][NF];
-      auto read_a = [&](bf16x8_t (&dst)[NF], int t) {
-        const int c = 16 * jj + 4 * g + t;  // K = 128 j + 32 g + 8 t .. + 7
-#pragma unroll
-        for (int f = 0; f < NF; ++f) {
-          const int row = 16 * f + c16;
-          dst[f] = *reinterpret_cast<const bf16x8_t*>(xs + (row * RCH + (c ^ (row & 15))) * 16);
-        }
-      };
-      read_a(a[0], 0);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        if (t < 3) read_a(a[(t + 1) & 1], t + 1);
-        bf16x8_t bq[CT];
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-          const float sc = t < 2 ? decode_e4m3<0>(sv[i][ct]) : decode_e4m3<1>(sv[i][ct]);
-          bq[ct] = dequant8(wv[i][ct][t], sc);
-        }
-#pragma unroll
-        for (int f = 0; f < NF; ++f)
-#pragma unroll
-          for (int ct = 0; ct < CT; ++ct)
-            acc[f][ct] =
-                __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[t & 1][f], bq[ct], acc[f][ct], 0, 0, 0);
-      }
+    for (int ct = 0; ct < CT; ++ct) {
+      const float sc = t < 2 ? decode_e4m3<0>(sv[i][ct]) : decode_e4m3<1>(sv[i][ct]);
+      bq[ct] = dequant8(wv[i][ct][t], sc);
     }
-    if (more) {
-      __syncthreads();  // every wave is done with this phase's rows
-      if (!kPrefetch) load_phase(ph + 1);
-      store_phase();
-      __syncthreads();
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+        acc[f][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[f], bq[ct], acc[f][ct], 0, 0, 0);
+  };
+  // multiply out group i of this wave (token rows in region slot sl)
+  auto group = [&](int i, int sl) {
+    const uint8_t* xg = region + sl * GB;
+    // A fragments of step t + 1 are read while step t is dequantized and
+    // multiplied (LDS latency behind the MFMAs)
+    bf16x8_t a[2][NF];
+    auto read_a = [&](bf16x8_t (&dst)[NF], int t) {
+      const int c = 4 * g + t;  // K = 128 j + 32 g + 8 t .. + 7
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const int row = 16 * f + c16;
+        dst[f] = *reinterpret_cast<const bf16x8_t*>(xg + (row * 16 + (c ^ (row & 15))) * 16);
+      }
+    };
+    read_a(a[0], 0);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if (t < 3) read_a(a[(t + 1) & 1], t + 1);
+      mma_step(i, t, a[t & 1]);
+    }
+  };
+  // Only this wave reads its region, so it waits for its own loads alone:
+  // after the first group's token rows come the second group's (when both
+  // are resident) and the 2 CT weight and scale loads of each group.
+  constexpr int kWLoads = GPW * CT * 2;
+  if constexpr (RES == GPW) {
+    if (wave < ng) {  // wave-uniform
+      wait_vmcnt_c<XL + kWLoads>();
+      group(0, 0);
+    }
+    if (wave + kGemvWaves < ng) {
+      wait_vmcnt_c<kWLoads>();
+      group(1, 1);
+    }
+  } else if (wave < ng) {
+    wait_vmcnt_c<kWLoads>();
+    group(0, 0);
+    if (wave + kGemvWaves < ng) {
+      // the second group replaces the first in the region, once this wave's
+      // reads of it are done (holding all of the first group's fragments in
+      // registers, to load the second one sooner, spills at 48 and 64 rows)
+      wait_lgkmcnt0();
+      load_group(wave + kGemvWaves, 0);
+      wait_vmcnt_c<0>();
+      group(1, 0);
     }
   }
+
+  // every token-row load of this wave has landed (those of groups past the
+  // unit write zeros) before the regions are reused below
+  wait_vmcnt_c<0>();
 
   // Sum the waves in a fixed order, (((w0 + w4) + (w1 + w5)) + (w2 + w6)) +
   // (w3 + w7): waves 4..7 hand their sums to waves 0..3, which publish the

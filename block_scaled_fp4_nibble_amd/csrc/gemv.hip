@@ -310,6 +310,10 @@ __global__ __launch_bounds__(kGemvThreads) void decode_sk_kernel(GemmParams p) {
   static_assert(kDskCols % 16 == 0 && kDskMaxGroups % kGemvWaves == 0, "unit shape");
   static_assert(GPW == 2 && (RES == 1 || RES == GPW), "a wave's groups: one or both resident");
   static_assert((kGemvWaves / 2) * NF * CT * 16 * kWave <= kGemvWaves * RES * GB, "exchange fits");
+  // a group's rows are whole 1 KB loads (four 256-byte rows each), and the
+  // waves' regions (RES groups each) fit the LDS set aside for them
+  static_assert(XL * 1024 == GB && BM % 4 == 0, "group rows per load");
+  static_assert(kGemvWaves * RES * GB <= kDskXBytes, "token-row regions fit");
   __shared__ __attribute__((aligned(16))) uint8_t xs[kGemvWaves * RES * GB];
   __shared__ int last_flag;
   const int tid = threadIdx.x, lane = tid & 63;

@@ -2,12 +2,14 @@
 k % 128 == 0) against the oracle.
 
 The kernel (gemv.hip, decode_sk_kernel) splits K into units of at most 16
-128-deep groups, stages the token rows in LDS in phases, sums the two K
-parities of a column tile through LDS and the splits through device-scope
-partial tiles in split order.  The cases cover one and several token-row
-phases, uneven and single splits (no workspace), column counts that are not
-a multiple of the 64-column unit, every row-fragment count and the decode
-shape of "The FP4 Frontier" (N = 4096, K = 7168) in full.  Tolerances as in
+128-deep groups; wave w owns the groups j with j % 8 == w and stages their
+token rows in an LDS region of its own (both of its groups up to 32 rows,
+one at a time above), the eight waves' sums meet through LDS and the splits
+through device-scope partial tiles in split order.  The cases cover both
+region layouts, units with fewer groups than waves (waves with nothing to
+multiply), uneven and single splits (no workspace), column counts that are
+not a multiple of the 64-column unit, every row-fragment count and the
+decode shape of "The FP4 Frontier" (N = 4096, K = 7168) in full.  Tolerances as in
 the other GEMM tests (FP32 output 1e-5, BF16 4e-3 of sum_k |x w|)."""
 import numpy as np
 import pytest
@@ -30,7 +32,7 @@ def decode_weight():
     return p, s, np.atleast_1d(g).astype(np.float32)
 
 
-@pytest.mark.parametrize("m", [17, 32, 48, 63, 64])
+@pytest.mark.parametrize("m", [9, 16, 17, 32, 33, 48, 63, 64])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 def test_decode_shape_rows(decode_weight, m, out_dtype):
     nv = require_gpu()
@@ -45,9 +47,9 @@ def test_decode_shape_rows(decode_weight, m, out_dtype):
     check_close(y, y_ref, d, "decode split-K m=%d" % m)
 
 
-# (m, n, k): ragged columns, one to 16 groups per unit, one to three token-row
-# phases (32 rows: 15 groups per phase; 64 rows: 7), a single split (at least
-# as many column tiles as CUs), 32 splits of one group
+# (m, n, k): ragged columns, one to 16 groups per unit (so some waves own no
+# group), both groups of a wave resident (up to 32 rows) or one at a time, a
+# single split (at least as many column tiles as CUs), 32 splits of one group
 SHAPES = [
     (5, 200, 384),
     (16, 64, 128),

@@ -1676,9 +1676,9 @@ static int env_int(const char* name, int dflt) {
 //      kLmMinRows rows; NVFP4_LM=0 disables it)
 //   4  K-phase kernel, 4 waves x 64 columns (dense, up to 16 rows)
 //   6  dot-product kernel (dense, one to four rows; gemv.hip)
-//   7  one MFMA row tile per 16 columns, whole K (dense, 5 to 8 rows, to 16
+//   7  one MFMA row tile per 16 columns, whole K (dense, 5 and 6 rows, to 16
 //      with NVFP4_DSK=0; gemv.hip)
-//   8  split-K decode kernel, 64 columns per unit (dense, 9 to 64 rows, or
+//   8  split-K decode kernel, 64 columns per unit (dense, 7 to 64 rows, or
 //      5 to 64 with NVFP4_DSK=2; NVFP4_DSK=0 disables it; gemv.hip)
 constexpr int kLmMinRows = 256;
 constexpr int kMinSplitStages = 7;
@@ -1767,16 +1767,16 @@ GemmPlan plan_gemm(int64_t rows, int64_t num_experts, int64_t n, int64_t k, bool
     pl.ws_bytes = 0;
     return pl;
   }
-  // 9 to 64 dense rows, k % 128 == 0: split-K decode kernel, 64 columns per
+  // 7 to 64 dense rows, k % 128 == 0: split-K decode kernel, 64 columns per
   // unit, each workgroup's weight share in flight at once (kind 8,
   // gemv.hip); the split count about fills the CUs with units.  At N = 4096,
-  // K = 7168 it takes 10.6 / 10.7 / 12.8 / 16.3 / 18.0 us at 12 / 16 / 32 /
-  // 48 / 64 rows against 11.3 / 12.6 us (kind 7, 12 / 16 rows) and 17.3 /
-  // 19-20 / 20 us (K-phase kernel, 32 / 48 / 64 rows); at 8 rows kind 7 is
-  // faster (10.3 against 10.8 us)
+  // K = 7168 it takes 9.6 / 9.6 / 9.7 / 11.2 / 14.0 / 15.7 us at 7 / 12 / 16 /
+  // 32 / 48 / 64 rows, against 10.0 us for kind 7 at 7 and 8 rows and 17.3 /
+  // 19-20 / 20 us for the K-phase kernel at 32 / 48 / 64 rows; at 5 rows
+  // kind 7 is faster (9.2 against 9.5 us), at 6 they are level
   const int dsk = env_int("NVFP4_DSK", 1);
   if (!grouped && rows > kGemvMaxRows && rows <= 64 && k % 128 == 0 &&
-      env_int("NVFP4_GEMV", 1) != 0 && (dsk == 2 || (dsk == 1 && rows > 8))) {
+      env_int("NVFP4_GEMV", 1) != 0 && (dsk == 2 || (dsk == 1 && rows > 6))) {
     const int64_t n_tiles = (n + kDskCols - 1) / kDskCols;
     const int64_t groups = k / 128;
     int64_t splits = std::min<int64_t>(groups, std::max<int64_t>(1, cu_count / n_tiles));

@@ -1,5 +1,5 @@
 // gemv.hip -- dense decode products: one to four token rows (gemv_kernel),
-// 5 to 8 rows (decode_mfma_kernel) and 9 to 64 rows (decode_sk_kernel).
+// 5 and 6 rows (decode_mfma_kernel) and 7 to 64 rows (decode_sk_kernel).
 //
 // One to four rows:
 //
@@ -170,7 +170,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemmParams p) {
   }
 }
 
-// ---- 5 to 8 rows: one MFMA row tile, whole K per workgroup --------------------
+// ---- 5 and 6 rows: one MFMA row tile, whole K per workgroup ------------------
 //
 // Above four rows the per-row dot products cost more than one BF16 MFMA row
 // tile, but the K-phase kernel's latency structure (a ring of 128-deep stages,
@@ -256,7 +256,7 @@ __global__ __launch_bounds__(kGemvThreads) void decode_mfma_kernel(GemmParams p)
   }
 }
 
-// ---- 9 to 64 rows: split K, a workgroup's whole weight share in flight --------
+// ---- 7 to 64 rows: split K, a workgroup's whole weight share in flight --------
 //
 // Decode moves each weight byte once, and with a few dozen rows the per-CU
 // weight share is a few tens of KB: the time is about one HBM latency plus

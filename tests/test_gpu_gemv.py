@@ -4,11 +4,12 @@ Decode products ("The FP4 Frontier", Finding 7: bandwidth-bound at small
 batch) with at most four token rows run on a kernel that keeps the block
 scale out of the inner loop: per 16-element block the exact E2M1 values are
 dotted with the activations in FP32, and the block's E4M3 scale multiplies
-that partial sum.  Five to eight rows (k % 128 == 0) run on one MFMA row
+that partial sum.  Five and six rows (k % 128 == 0) run on one MFMA row
 tile per 16 columns with whole K per workgroup and a permuted K order inside
-each MFMA; from nine rows the split-K decode kernel takes over (its own
-tests are in test_gpu_decode_sk.py; the 13- and 16-row cases here run on it,
-with up to 128 splits of one K group at K = 16384).  Same tolerances as
+each MFMA; from seven rows the split-K decode kernel takes over (its own
+tests are in test_gpu_decode_sk.py; the 8-, 13- and 16-row cases here run
+on it, with up to 128 splits of one K group at K = 16384, and again on the
+MFMA kernel, which NVFP4_DSK=0 extends to 16 rows).  Same tolerances as
 every GEMM: FP32 output within 1e-5, BF16 within 4e-3 of sum_k |x * w|."""
 import os
 
@@ -98,6 +99,10 @@ def test_mfma_rows_against_oracle(m, n, k):
     qw = to_qw(nv, p, s, g)
     check_close(run_gemm(nv, x, qw, torch.float32), y_ref, d, "f32 %dx%dx%d" % (m, n, k))
     check_close(run_gemm(nv, x, qw, torch.bfloat16), y_ref, d, "bf16 %dx%dx%d" % (m, n, k))
+    with env("NVFP4_DSK", "0"):  # the whole-K MFMA kernel up to 16 rows
+        name = nv.load_library().nvfp4_kernel_name(m, 1, n, k, 0, 0).decode()
+        assert name.startswith("nvfp4::decode_mfma_kernel<"), name
+        check_close(run_gemm(nv, x, qw, torch.float32), y_ref, d, "mfma f32 %dx%dx%d" % (m, n, k))
 
 
 @pytest.fixture(scope="module")

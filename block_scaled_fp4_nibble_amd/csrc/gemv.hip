@@ -309,7 +309,6 @@ __global__ __launch_bounds__(kGemvThreads) void decode_sk_kernel(GemmParams p) {
   constexpr int XL = GB / 1024;                      // 1 KB loads per group
   static_assert(kDskCols % 16 == 0 && kDskMaxGroups % kGemvWaves == 0, "unit shape");
   static_assert(GPW == 2 && (RES == 1 || RES == GPW), "a wave's groups: one or both resident");
-  static_assert((kGemvWaves / 2) * NF * CT * 16 * kWave <= kGemvWaves * RES * GB, "exchange fits");
   // a group's rows are whole 1 KB loads (four 256-byte rows each), and the
   // waves' regions (RES groups each) fit the LDS set aside for them
   static_assert(XL * 1024 == GB && BM % 4 == 0, "group rows per load");
@@ -450,36 +449,28 @@ __global__ __launch_bounds__(kGemvThreads) void decode_sk_kernel(GemmParams p) {
   wait_vmcnt_c<0>();
 
   // Sum the waves in a fixed order, (((w0 + w4) + (w1 + w5)) + (w2 + w6)) +
-  // (w3 + w7): waves 4..7 hand their sums to waves 0..3, which publish the
-  // four pair sums, and then every thread adds the four, in that order, for
-  // its share of the tile (float4 q = (f CT + ct) 64 + lane of the
-  // accumulator layout) -- all 512 threads at once, not one wave.
+  // (w3 + w7): each wave publishes its sums at the start of its own region
+  // (which no other wave reads, so it needs no barrier first), and after one
+  // barrier every thread adds the eight, in that order, for its share of the
+  // tile (float4 q = (f CT + ct) 64 + lane of the accumulator layout) -- all
+  // 512 threads at once, not one wave.
   constexpr int Q = NF * CT * kWave;                            // float4 values per tile
   constexpr int QPT = (Q + kGemvThreads - 1) / kGemvThreads;    // per thread: 1 or 2
-  f32x4_t* xch = reinterpret_cast<f32x4_t*>(xs);
-  auto put = [&](int slot) {
+  static_assert(Q * 16 <= RES * GB, "a wave's sums fit its region");
+  auto slot = [&](int w) { return reinterpret_cast<f32x4_t*>(xs + w * (RES * GB)); };
 #pragma unroll
-    for (int f = 0; f < NF; ++f)
+  for (int f = 0; f < NF; ++f)
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) xch[slot * Q + (f * CT + ct) * kWave + lane] = acc[f][ct];
-  };
-  __syncthreads();
-  if (wave >= 4) put(wave - 4);
-  __syncthreads();
-  if (wave < 4) {
-#pragma unroll
-    for (int f = 0; f < NF; ++f)
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
-        acc[f][ct] = acc[f][ct] + xch[wave * Q + (f * CT + ct) * kWave + lane];
-    put(wave);
-  }
+    for (int ct = 0; ct < CT; ++ct) slot(wave)[(f * CT + ct) * kWave + lane] = acc[f][ct];
   __syncthreads();
   f32x4_t sum[QPT];
 #pragma unroll
   for (int i = 0; i < QPT; ++i) {
     const int q = tid + i * kGemvThreads;
-    if (q < Q) sum[i] = ((xch[q] + xch[Q + q]) + xch[2 * Q + q]) + xch[3 * Q + q];
+    if (q < Q)
+      sum[i] = (((slot(0)[q] + slot(4)[q]) + (slot(1)[q] + slot(5)[q])) +
+                (slot(2)[q] + slot(6)[q])) +
+               (slot(3)[q] + slot(7)[q]);
   }
   // float4 q of the accumulator layout -> its 4 elements of the row-major
   // FP32 tile in LDS (rows 16 f + 4 g + r, column 16 ct + l % 16)

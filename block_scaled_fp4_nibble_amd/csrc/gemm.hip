@@ -1675,9 +1675,10 @@ static int env_int(const char* name, int dflt) {
 //   3  large-M kernel, 256 x 256 tiles (dense products with at least
 //      kLmMinRows rows; NVFP4_LM=0 disables it)
 //   4  K-phase kernel, 4 waves x 64 columns (dense, up to 16 rows)
-//   6  dot-product kernel (dense, one to four rows; gemv.hip)
-//   7  one MFMA row tile per 16 columns, whole K (dense, 5 and 6 rows, to 16
-//      with NVFP4_DSK=0; gemv.hip)
+//   6  dot-product kernel (dense, one to six rows; gemv.hip)
+//   7  one MFMA row tile per 16 columns, whole K (dense, 5 and 6 rows whose
+//      K is too long for kind 6, and 7 to 16 rows with NVFP4_DSK=0 or where
+//      kind 8's counters cannot hold the column tiles; gemv.hip)
 //   8  split-K decode kernel, 64 columns per unit (dense, 7 to 64 rows, or
 //      5 to 64 with NVFP4_DSK=2; NVFP4_DSK=0 disables it; gemv.hip)
 constexpr int kLmMinRows = 256;
@@ -1751,9 +1752,13 @@ GemmPlan plan_gemm(int64_t rows, int64_t num_experts, int64_t n, int64_t k, bool
                    int cu_count, bool allow_split) {
   GemmPlan pl{};
   pl.fast = (k % 64) == 0;
-  // one to four dense rows: the dot-product kernel, 16 columns per workgroup,
-  // whole K, no workspace (kind 6)
-  if (!grouped && rows >= 1 && rows <= kGemvMaxRows && k % 32 == 0 &&
+  // one to six dense rows: the dot-product kernel, 16 columns per workgroup,
+  // whole K, no workspace (kind 6).  At N = 4096, K = 7168 it takes 8.2 /
+  // 9.1 us at 5 / 6 rows against 9.3 / 9.6 us for kind 7
+  // NVFP4_DSK=2 (tuning): the split-K decode kernel from five rows
+  const int dsk = env_int("NVFP4_DSK", 1);
+  const int gemv_rows = dsk == 2 ? 4 : kGemvMaxRows;
+  if (!grouped && rows >= 1 && rows <= gemv_rows && k % 32 == 0 &&
       rows * k * 2 <= kGemvMaxXBytes && env_int("NVFP4_GEMV", 1) != 0) {
     pl.kind = 6;
     pl.bm = (int)rows;
@@ -1772,11 +1777,11 @@ GemmPlan plan_gemm(int64_t rows, int64_t num_experts, int64_t n, int64_t k, bool
   // gemv.hip); the split count about fills the CUs with units.  At N = 4096,
   // K = 7168 it takes 9.6 / 9.6 / 9.7 / 11.2 / 14.0 / 15.7 us at 7 / 12 / 16 /
   // 32 / 48 / 64 rows, against 10.0 us for kind 7 at 7 and 8 rows and 17.3 /
-  // 19-20 / 20 us for the K-phase kernel at 32 / 48 / 64 rows; at 5 rows
-  // kind 7 is faster (9.2 against 9.5 us), at 6 they are level
-  const int dsk = env_int("NVFP4_DSK", 1);
-  if (!grouped && rows > kGemvMaxRows && rows <= 64 && k % 128 == 0 &&
-      env_int("NVFP4_GEMV", 1) != 0 && (dsk == 2 || (dsk == 1 && rows > 6))) {
+  // 19-20 / 20 us for the K-phase kernel at 32 / 48 / 64 rows
+  // (rows of five and six reach here only when the dot-product kernel cannot
+  // stage them: a long K, or NVFP4_DSK=2)
+  if (!grouped && rows > 4 && rows <= 64 && k % 128 == 0 && env_int("NVFP4_GEMV", 1) != 0 &&
+      (dsk == 2 || (dsk == 1 && rows > 6))) {
     const int64_t n_tiles = (n + kDskCols - 1) / kDskCols;
     const int64_t groups = k / 128;
     int64_t splits = std::min<int64_t>(groups, std::max<int64_t>(1, cu_count / n_tiles));
@@ -1801,7 +1806,7 @@ GemmPlan plan_gemm(int64_t rows, int64_t num_experts, int64_t n, int64_t k, bool
   }
   // five to sixteen dense rows, k % 128 == 0: one MFMA row tile per 16
   // columns, whole K, every load in flight at once (kind 7, gemv.hip)
-  if (!grouped && rows > kGemvMaxRows && rows <= 16 && k % 128 == 0 &&
+  if (!grouped && rows > 4 && rows <= 16 && k % 128 == 0 &&
       env_int("NVFP4_GEMV", 1) != 0) {
     pl.kind = 7;
     pl.bm = 16;
@@ -1887,8 +1892,9 @@ bool plan_pairs_tiles(const GemmPlan& pl) {
 const char* plan_kernel_name(const GemmPlan& pl, bool gather) {
   if (pl.kind == 6) {
     static const char* kGemv[] = {"nvfp4::gemv_kernel<1>", "nvfp4::gemv_kernel<2>",
-                                  "nvfp4::gemv_kernel<3>", "nvfp4::gemv_kernel<4>"};
-    return kGemv[std::min(std::max(pl.bm, 1), 4) - 1];
+                                  "nvfp4::gemv_kernel<3>", "nvfp4::gemv_kernel<4>",
+                                  "nvfp4::gemv_kernel<5>", "nvfp4::gemv_kernel<6>"};
+    return kGemv[std::min(std::max(pl.bm, 1), kGemvMaxRows) - 1];
   }
   if (pl.kind == 7) {
     // the template argument is the number of 128-deep K groups per wave

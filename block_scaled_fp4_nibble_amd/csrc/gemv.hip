@@ -1,7 +1,9 @@
-// gemv.hip -- dense decode products: one to four token rows (gemv_kernel),
-// 5 and 6 rows (decode_mfma_kernel) and 7 to 64 rows (decode_sk_kernel).
+// gemv.hip -- dense decode products: one to six token rows (gemv_kernel) and
+// 7 to 64 rows (decode_sk_kernel); decode_mfma_kernel serves five and six
+// rows whose K is too long to stage, and 7 to 16 rows when the split-K
+// kernel is switched off or its counters would not hold the column tiles.
 //
-// One to four rows:
+// One to six rows:
 //
 // Decode is the bandwidth-bound case ("The FP4 Frontier", Finding 7).  With
 // so few rows a 16-row MFMA tile is mostly padding, and the in-register
@@ -170,9 +172,9 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemmParams p) {
   }
 }
 
-// ---- 5 and 6 rows: one MFMA row tile, whole K per workgroup ------------------
+// ---- one MFMA row tile, whole K per workgroup (up to 16 rows) -----------------
 //
-// Above four rows the per-row dot products cost more than one BF16 MFMA row
+// With many rows the per-row dot products cost more than one BF16 MFMA row
 // tile, but the K-phase kernel's latency structure (a ring of 128-deep stages,
 // split K with a partial-tile hand-off) still dominates at decode sizes.  This
 // kernel keeps every load of a workgroup in flight at once instead: one
@@ -618,6 +620,8 @@ hipError_t launch_gemv(const GemmPlan& pl, const GemmParams& p, hipStream_t stre
     case 2: hipLaunchKernelGGL(gemv_kernel<2>, grid, block, pl.dyn_lds, stream, p); break;
     case 3: hipLaunchKernelGGL(gemv_kernel<3>, grid, block, pl.dyn_lds, stream, p); break;
     case 4: hipLaunchKernelGGL(gemv_kernel<4>, grid, block, pl.dyn_lds, stream, p); break;
+    case 5: hipLaunchKernelGGL(gemv_kernel<5>, grid, block, pl.dyn_lds, stream, p); break;
+    case 6: hipLaunchKernelGGL(gemv_kernel<6>, grid, block, pl.dyn_lds, stream, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

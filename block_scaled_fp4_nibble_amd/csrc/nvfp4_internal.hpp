@@ -75,13 +75,13 @@ struct GemmPlan {
 
 // Dense products of at most kGemvMaxRows rows with k % 32 == 0 run on the
 // dot-product kernel (gemv.hip), which stages the rows in LDS (at most
-// kGemvMaxXBytes).
-constexpr int kGemvMaxRows = 4;
+// kGemvMaxXBytes: six rows of K = 8192).
+constexpr int kGemvMaxRows = 6;
 // Both decode kernels run 8-wave workgroups.
 constexpr int kGemvThreads = 512;
 constexpr int kGemvWaves = kGemvThreads / 64;
-constexpr int64_t kGemvMaxXBytes = 65536;
-// Dense products of 5 to 64 rows with k % 128 == 0 run on the split-K decode
+constexpr int64_t kGemvMaxXBytes = 98304;
+// Dense products of 7 to 64 rows with k % 128 == 0 run on the split-K decode
 // kernel (gemv.hip): units of kDskCols output columns by at most
 // kDskMaxGroups 128-deep K groups.
 constexpr int kDskCols = 64;

@@ -63,7 +63,7 @@ def act(m, k, family, seed):
 # (kind, m, n, k, overrides)
 DENSE_KINDS = [
     (6, 3, 200, 512, {}),
-    (7, 6, 200, 1024, {}),
+    (7, 7, 200, 1024, {"NVFP4_DSK": 0}),
     (8, 11, 200, 1024, {}),
     (8, 40, 300, 1024, {}),
     (4, 9, 200, 1024, {"NVFP4_GEMV": 0}),

@@ -4,12 +4,13 @@ Decode products ("The FP4 Frontier", Finding 7: bandwidth-bound at small
 batch) with at most four token rows run on a kernel that keeps the block
 scale out of the inner loop: per 16-element block the exact E2M1 values are
 dotted with the activations in FP32, and the block's E4M3 scale multiplies
-that partial sum.  Five and six rows (k % 128 == 0) run on one MFMA row
-tile per 16 columns with whole K per workgroup and a permuted K order inside
-each MFMA; from seven rows the split-K decode kernel takes over (its own
-tests are in test_gpu_decode_sk.py; the 8-, 13- and 16-row cases here run
-on it, with up to 128 splits of one K group at K = 16384, and again on the
-MFMA kernel, which NVFP4_DSK=0 extends to 16 rows).  Same tolerances as
+that partial sum; it takes up to six rows while their K fits its LDS.  Five
+and six rows of longer K (k % 128 == 0) run on one MFMA row tile per 16
+columns with whole K per workgroup and a permuted K order inside each MFMA
+(the K = 16384 cases below); from seven rows the split-K decode kernel takes
+over (its own tests are in test_gpu_decode_sk.py; the 8-, 13- and 16-row
+cases here run on it, with up to 128 splits of one K group at K = 16384, and
+again on the MFMA kernel, which NVFP4_DSK=0 extends to 16 rows).  Same tolerances as
 every GEMM: FP32 output within 1e-5, BF16 within 4e-3 of sum_k |x * w|."""
 import os
 
@@ -65,10 +66,12 @@ SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("m", [1, 2, 3, 4])
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 6])
 @pytest.mark.parametrize("n,k", SHAPES)
 def test_against_oracle(m, n, k):
     nv = require_gpu()
+    name = nv.load_library().nvfp4_kernel_name(m, 1, n, k, 0, 0).decode()
+    assert name == "nvfp4::gemv_kernel<%d>" % m, name
     key = m * 1000003 + n * 1009 + k
     w = W.normal_bf16((n, k), 0.05, (81, key, 0))
     x = W.normal_bf16((m, k), 1.0, (81, key, 1))
@@ -87,7 +90,7 @@ SHAPES_128 = [
 ]
 
 
-@pytest.mark.parametrize("m", [5, 8, 13, 16])
+@pytest.mark.parametrize("m", [5, 6, 8, 13, 16])
 @pytest.mark.parametrize("n,k", SHAPES_128)
 def test_mfma_rows_against_oracle(m, n, k):
     nv = require_gpu()
@@ -99,6 +102,8 @@ def test_mfma_rows_against_oracle(m, n, k):
     qw = to_qw(nv, p, s, g)
     check_close(run_gemm(nv, x, qw, torch.float32), y_ref, d, "f32 %dx%dx%d" % (m, n, k))
     check_close(run_gemm(nv, x, qw, torch.bfloat16), y_ref, d, "bf16 %dx%dx%d" % (m, n, k))
+    if m <= 6 and m * k * 2 <= 98304:
+        return  # the dot-product kernel's (staged rows fit its LDS)
     with env("NVFP4_DSK", "0"):  # the whole-K MFMA kernel up to 16 rows
         name = nv.load_library().nvfp4_kernel_name(m, 1, n, k, 0, 0).decode()
         assert name.startswith("nvfp4::decode_mfma_kernel<"), name

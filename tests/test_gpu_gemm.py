@@ -37,9 +37,10 @@ def run_gemm(nv, x_bits, qw, out_dtype, sentinel=True):
 
 @pytest.fixture
 def splitk(request):
-    """Force a K split through the library's tuning override (and the K-phase
-    kernel for products of one to four rows, which otherwise take the
-    dot-product kernel and never split K)."""
+    """Force a K split through the library's tuning override, on the K-phase
+    kernel also for products of 1 to 64 rows (the decode kernels, which
+    otherwise take them, are switched off: they split K by their own plan or
+    not at all)."""
     old = {v: os.environ.get(v) for v in ("NVFP4_SPLITK", "NVFP4_GEMV")}
     os.environ["NVFP4_SPLITK"] = str(request.param)
     os.environ["NVFP4_GEMV"] = "0"

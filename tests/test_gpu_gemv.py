@@ -1,10 +1,10 @@
 """GPU parity of the decode kernels for dense products of one to sixteen rows.
 
 Decode products ("The FP4 Frontier", Finding 7: bandwidth-bound at small
-batch) with at most four token rows run on a kernel that keeps the block
-scale out of the inner loop: per 16-element block the exact E2M1 values are
-dotted with the activations in FP32, and the block's E4M3 scale multiplies
-that partial sum; it takes up to six rows while their K fits its LDS.  Five
+batch) of one to six token rows whose K fits its LDS (rows x K x 2 bytes up
+to 96 KB) run on a kernel that keeps the block scale out of the inner loop:
+per 16-element block the exact E2M1 values are dotted with the activations
+in FP32, and the block's E4M3 scale multiplies that partial sum.  Five
 and six rows of longer K (k % 128 == 0) run on one MFMA row tile per 16
 columns with whole K per workgroup and a permuted K order inside each MFMA
 (the K = 16384 cases below); from seven rows the split-K decode kernel takes

@@ -7,9 +7,10 @@ included.  Each family below is run through each kernel the planner can pick,
 forced with the library's tuning overrides, with FP32 output (tolerance 1e-5
 of sum_k |x w|):
 
-  kind 6  dot-product kernel (1-4 dense rows)
-  kind 7  MFMA decode kernel (5-8 dense rows, k % 128 == 0)
-  kind 8  split-K decode kernel (9-64 dense rows, k % 128 == 0)
+  kind 6  dot-product kernel (1-6 dense rows, rows x K x 2 bytes <= 96 KB)
+  kind 7  MFMA decode kernel (5-6 dense rows of longer K, k % 128 == 0;
+          up to 16 rows with NVFP4_DSK=0)
+  kind 8  split-K decode kernel (7-64 dense rows, k % 128 == 0)
   kind 4  K-phase kernel, 64-column tiles (dense <= 16 rows, NVFP4_GEMV=0)
   kind 1  K-phase kernel, 4 waves x 128 columns (65-128 dense rows, 17-64
           with NVFP4_DSK=0, or a grouped launch with <= 32 rows per expert)

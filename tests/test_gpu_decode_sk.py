@@ -1,5 +1,5 @@
-"""GPU parity of the split-K decode kernel (dense products of 5 to 64 rows,
-k % 128 == 0) against the oracle.
+"""GPU parity of the split-K decode kernel (dense products of 7 to 64 rows,
+and of 5 and 6 with NVFP4_DSK=2; k % 128 == 0) against the oracle.
 
 The kernel (gemv.hip, decode_sk_kernel) splits K into units of at most 16
 128-deep groups; wave w owns the groups j with j % 8 == w and stages their

@@ -144,7 +144,7 @@ def test_zero_weight_gives_exact_zero():
 
 
 def test_rows_beyond_lds_limit_use_the_kphase_kernel():
-    # 4 rows x K = 16384 is 128 KB of activations, above the 64 KB the
+    # 4 rows x K = 16384 is 128 KB of activations, above the 96 KB the
     # dot-product kernel stages; the product still comes out right
     nv = require_gpu()
     w = W.normal_bf16((96, 16384), 0.05, (81, 2, 0))
